@@ -1,0 +1,109 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin fails.
+
+Each case swaps one piece of the oracle for a wrong variant -- an off-by-one
+mask, a wrong KV-head index, a transposed V block, a dropped rescale, a wrong
+exponent bias, the last instead of the first maximum, an AL off by one -- and
+runs the pin that should catch it.  The real oracle is restored afterwards.
+"""
+import numpy as np
+import pytest
+
+import oracle.accept as acc
+import oracle.attention as att
+import oracle.formats as fmt
+from tests import test_oracle_accept as T_acc
+from tests import test_oracle_attention as T_att
+from tests import test_oracle_formats as T_fmt
+from workloads import MINI
+
+
+def _expect_pin_failure(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_mask_off_by_one_is_caught(monkeypatch):
+    # position i no longer sees itself
+    monkeypatch.setattr(att, "_visible",
+                        lambda R, L: np.arange(L)[None, :] < (L - R + np.arange(R))[:, None])
+    _expect_pin_failure(T_att.test_oracle_matches_torch_sdpa, MINI["mini_gqa4_d7"])
+
+
+def test_wrong_kv_head_is_caught(monkeypatch):
+    real = att.gather_kv
+
+    def swapped(*a):
+        K, V = real(*a)
+        return K[:, ::-1], V[:, ::-1]
+    monkeypatch.setattr(att, "gather_kv", swapped)
+    _expect_pin_failure(T_att.test_oracle_matches_torch_sdpa, MINI["mini_gqa4_d7"])
+
+
+def test_transposed_v_block_is_caught(monkeypatch):
+    def wrong_gather(k_cache, v_cache, k_scale, v_scale, block_table, b, L):
+        nb = -(-int(L) // 16)
+        blocks = np.asarray(block_table[b, :nb], dtype=np.int64)
+        kb = k_cache[blocks]
+        n, H, nx, bs, X = kb.shape
+        K = att._decode(kb.transpose(0, 3, 1, 2, 4).reshape(nb * 16, H, nx * X)[:L])
+        # reads V as if it were token-major [16][hd] inside each block
+        vb = v_cache[blocks].reshape(nb, H, 16, -1)
+        V = att._decode(vb.transpose(0, 2, 1, 3).reshape(nb * 16, H, -1)[:L])
+        return K, V
+    monkeypatch.setattr(att, "gather_kv", wrong_gather)
+    _expect_pin_failure(T_att.test_oracle_matches_torch_sdpa, MINI["mini_gqa4_d7"])
+
+
+def test_dropped_rescale_is_caught(monkeypatch):
+    def no_rescale(s, v, tile):
+        n, L = s.shape
+        O = np.zeros((n, v.shape[1])); m = np.full(n, -np.inf); l = np.zeros(n)
+        for t0 in range(0, L, tile):
+            st = s[:, t0:t0 + tile]
+            m_new = np.maximum(m, st.max(axis=1))
+            p = np.exp(st - m_new[:, None])
+            l = l + p.sum(axis=1)          # missing l * exp(m - m_new)
+            O = O + p @ v[t0:t0 + tile]    # missing O * exp(m - m_new)
+            m = m_new
+        return O, m, l
+    monkeypatch.setattr(att, "online_softmax_rows", no_rescale)
+    _expect_pin_failure(T_att.test_online_softmax_equals_full_softmax, "mini_gqa4_d7",
+                        (64,), (None,))
+
+
+def test_wrong_e4m3_bias_is_caught(monkeypatch):
+    def bias8(bits):
+        b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+        s, e, m = (b >> 7) & 1, (b >> 3) & 0xF, b & 7
+        sign = np.where(s == 1, -1.0, 1.0)
+        v = np.where(e == 0, sign * np.ldexp(m / 8.0, -7), sign * np.ldexp(1 + m / 8.0, e - 8))
+        return np.where((e == 15) & (m == 7), np.nan, v)
+    monkeypatch.setattr(T_fmt, "e4m3_bits_to_f64", bias8)
+    _expect_pin_failure(T_fmt.test_e4m3_all_codes_match_torch)
+
+
+def test_last_maximum_is_caught(monkeypatch):
+    def last_max(x):
+        x = np.asarray(x, np.float32)
+        return (x.shape[-1] - 1 - np.argmax(x[..., ::-1], axis=-1)).astype(np.int32)
+    monkeypatch.setattr(T_acc, "oracle_argmax", last_max)
+    _expect_pin_failure(T_acc.test_argmax_exhaustive_small, 3)
+
+
+def test_accept_len_off_by_one_is_caught(monkeypatch):
+    real = acc.oracle_accept
+
+    def short(*a):
+        r = real(*a)
+        r["accept_len"] = np.maximum(r["accept_len"] - 1, 0)
+        return r
+    monkeypatch.setattr(T_acc, "oracle_accept", short)
+    _expect_pin_failure(T_acc.test_prefix_exhaustive, 2)
+
+
+def test_bf16_half_shift_is_caught(monkeypatch):
+    def wrong(bits):
+        u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+        return u.view(np.float32).astype(np.float64)
+    monkeypatch.setattr(T_fmt, "bf16_bits_to_f64", wrong)
+    _expect_pin_failure(T_fmt.test_bf16_all_patterns_match_torch)
