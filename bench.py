@@ -1,0 +1,262 @@
+"""Benchmark of the verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--split-tokens S] [--no-cpu-baseline]
+
+One step = one full pass of the hot path over one batch: spec_verify_attn
+(paged GQA attention of the 1 + D verified positions, split-K merge) followed
+by spec_accept (vocab argmax, first-mismatch prefix, KV-length commit), both
+through the C ABI on the same stream, with all inputs already in HBM.
+
+Printed: one JSON line with the metric (verified tokens/s = sum of acceptance
+lengths per step / step time), the attention kernel's achieved HBM bandwidth
+against the MI355X peak (the roofline object), the MFMA rate, and the oracle's
+throughput on a bounded sample on the host cores (the cpu_baseline object).
+The default workload is the 70B-like layer: B=32, H_q=64, H_kv=8, hd=128,
+D=15 (G*(1+D) = 128), ragged context T ~ U[2048, 32768], bf16 paged KV,
+acceptance over fp32 logits [32, 16, 128256].
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "verified tokens/sec + KV HBM GB/s (% peak) at Llama-70B-like GQA, D=15"
+KERNEL_SOURCES = ("speculative_decoding_verification_15_amd/csrc/sv_attn.hip",
+                  "speculative_decoding_verification_15_amd/csrc/sv_device.h",
+                  "speculative_decoding_verification_15_amd/csrc/sv_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sv_attn.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def attn_algorithmic_bytes(inp) -> int:
+    """Bytes the attention must move at least once: every K and V element of the
+    L_b keys of each sequence, the fp8 scales of the blocks read, the block-table
+    entries, Q and the output."""
+    w = inp.w
+    L = inp.kv_lens.astype(np.int64)
+    elem = 1 if w.kv_dtype == "fp8_e4m3" else 2
+    kv = int(L.sum()) * w.H_kv * w.hd * 2 * elem
+    nblk = int(((L + 15) // 16).sum())
+    scales = nblk * w.H_kv * 2 * 4 if elem == 1 else 0
+    table = nblk * 4
+    qo = 2 * w.B * w.R * w.H_q * w.hd * 2
+    return kv + scales + table + qo
+
+
+def attn_algorithmic_kv_bytes(inp) -> int:
+    w = inp.w
+    elem = 1 if w.kv_dtype == "fp8_e4m3" else 2
+    return int(inp.kv_lens.astype(np.int64).sum()) * w.H_kv * w.hd * 2 * elem
+
+
+def attn_algorithmic_flops(inp) -> int:
+    """4 * M * hd flops per (visible key, KV head): QK^T and PV, unpadded M = G*(1+D),
+    counting every key of the sequence for every row (the causal tail is ignored)."""
+    w = inp.w
+    return int(inp.kv_lens.astype(np.int64).sum()) * w.H_kv * 4 * w.M * w.hd
+
+
+def read_traffic(src_hash):
+    """HBM traffic per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m = re.search(r"src_sha=(\w+).*?workload=(\S+).*?bytes_per_launch=(\d+)", txt, re.S)
+    if not m or m.group(1) != src_hash:
+        return None
+    return {"workload": m.group(2), "bytes": int(m.group(3))}
+
+
+def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
+    """Times the oracle (as it is) on whole sequences until ~budget_s of CPU work."""
+    from oracle.accept import oracle_accept
+    from oracle.attention import oracle_attn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    done, tokens, t_total = [], 0, 0.0
+    for b in range(w.B):
+        t0 = time.perf_counter()
+        oracle_attn(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale, inp.block_table,
+                    inp.kv_lens, D=w.D, H_kv=w.H_kv, sm_scale=w.sm_scale, seqs=[b])
+        res = oracle_accept(plan.logits[b:b + 1], draft[b:b + 1], inp.kv_lens[b:b + 1], w.D)
+        t_total += time.perf_counter() - t0
+        tokens += int(res["accept_len"][0])
+        done.append(b)
+        if t_total >= budget_s:
+            break
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {w.B} sequences (all {w.H_kv} KV heads): fp64 attention "
+                      f"+ acceptance, {t_total:.1f} s of host time, sum AL = {tokens}",
+            "seconds": round(t_total, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama31_70b_gqa8_d15")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_decoding_verification_15_amd as sv
+    from tests.gpu_util import DeviceAttn, attn_params, dev
+    from workloads import all_workloads, drafts_from_target, make_accept_plan, make_attn_inputs
+
+    w = all_workloads()[args.workload]
+    assert w.V > 0, "the benchmark step needs an acceptance vocabulary"
+    t_gen = time.perf_counter()
+    inp = make_attn_inputs(w)
+    logits_bytes = w.B * w.R * w.V * 4
+    n_sets = int(min(8, max(2, -(-512 * 2 ** 20 // logits_bytes))))
+    plan, logit_sets = make_accept_plan(w, n_logit_sets=n_sets)
+    # draft synthesis needs the target token of every row (input preparation)
+    target_host = np.argmax(plan.logits, axis=-1)
+    draft = drafts_from_target(plan, target_host)
+    t_gen = time.perf_counter() - t_gen
+
+    torch.cuda.set_device(0)
+    da = DeviceAttn(inp)
+    p = attn_params(inp, args.split_tokens)
+    ws_bytes = sv.spec_verify_attn_workspace_size(p)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty(da.q.shape, dtype=torch.int16, device="cuda")
+    lg = [dev(x) for x in logit_sets]
+    dr = dev(draft) if w.D > 0 else None
+    B, R, V, D = w.B, w.R, w.V, w.D
+    tgt = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    otok = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    kv_out = torch.empty((B,), dtype=torch.int32, device="cuda")
+    acc_ws_bytes = sv.spec_accept_workspace_size(B, D, V)
+    acc_ws = torch.empty(acc_ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sv.spec_verify_attn(p, da.q, da.k, da.v, da.ks, da.vs, da.bt, da.kl, out, ws, ws_bytes,
+                            stream=sh)
+        if ev is not None:
+            ev[1].record(stream)
+        sv.spec_accept(B, D, V, lg[i % n_sets], dr, tgt, al, otok, da.kl, kv_out, acc_ws,
+                       acc_ws_bytes, stream=sh)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sum_al = [int(al.cpu().sum())]   # AL of the last warm-up step (logit set (W-1) % n)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    t_attn = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_acc = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    # acceptance lengths of every logit set in use (the step cycles through them)
+    al_per_set = []
+    for j in range(n_sets):
+        sv.spec_accept(B, D, V, lg[j], dr, tgt, al, otok, da.kl, kv_out, acc_ws, acc_ws_bytes,
+                       stream=sh)
+        torch.cuda.synchronize()
+        al_per_set.append(int(al.cpu().sum()))
+    tokens_timed = sum(al_per_set[i % n_sets] for i in range(args.steps))
+
+    ms_per_step = total_ms / args.steps
+    value = tokens_timed / (total_ms / 1e3)
+    attn_us = float(np.mean(t_attn) * 1e3)
+    acc_us = float(np.mean(t_acc) * 1e3)
+    alg_bytes = attn_algorithmic_bytes(inp)
+    kv_bytes = attn_algorithmic_kv_bytes(inp)
+    achieved = alg_bytes / (attn_us * 1e-6) / 1e9
+    kv_gbps = kv_bytes / (attn_us * 1e-6) / 1e9
+    flops = attn_algorithmic_flops(inp)
+    tflops = flops / (attn_us * 1e-6) / 1e12
+    src_hash = kernel_source_hash()
+    tr = read_traffic(src_hash)
+    traffic = tr["bytes"] if tr and tr["workload"] == w.name else None
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/logits, permuted paged block table, "
+                "drafts matching the target argmax with per-sequence probability)",
+        "config": {
+            "workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "head_dim": w.hd,
+            "D": w.D, "M_rows_per_kv_head": w.M,
+            "context": (f"U[{w.T_range[0]},{w.T_range[1]}]" if w.T_range else w.T),
+            "sum_kv_len": int(inp.kv_lens.sum()), "kv_dtype": w.kv_dtype, "vocab": w.V,
+            "split_tokens": int(p.split_tokens) or "auto",
+            "logit_buffers_rotated": n_sets, "parallelism": "single GPU"},
+        "roofline": {
+            "kernel": "spec_verify_attn (sv_attn_partial + sv_attn_combine)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(attn_us, 2)},
+        "kv_hbm_GBps": round(kv_gbps, 1),
+        "kv_hbm_frac_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                 "algorithmic_flops_per_launch": flops},
+        "accept": {"avg_launch_us": round(acc_us, 2),
+                   "GBps": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9, 1)},
+        "sum_accept_len_per_step": round(tokens_timed / args.steps, 2),
+        "kernel_src_sha": src_hash,
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, plan, draft, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verification step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The verification step scores the D drafted tokens of each sequence plus one
+ * bonus position in a single target pass, then keeps the drafts up to the first
+ * one the target disagrees with.  Two calls cover it:
+ *
+ *   spec_verify_attn   attention of the R = D + 1 new positions of every
+ *                      sequence over its paged KV cache (GQA: G = H_q / H_kv
+ *                      query heads share one KV head, so G * R query rows read
+ *                      each KV head), with an online softmax and a split-K
+ *                      merge for long contexts.
+ *   spec_accept        per-row argmax of the target logits, first-mismatch
+ *                      prefix against the drafts, acceptance length and the
+ *                      committed KV length.
+ *
+ * Where the operations are defined (the pages this library implements):
+ *   - one target pass over the drafted positions plus the bonus position, and
+ *     the acceptance rule: "GPU and LLM", chapter 5 (animemo.app), section
+ *     "Speculative decoding (2): verify in one pass"; NVIDIA co-design summary
+ *     (papanda925.com), section "Basic structure of speculative decoding"
+ *     (draft length D, acceptance length AL in 1 .. 1 + D);
+ *   - the running max / running sum softmax: "GPU and LLM" ch. 5, section
+ *     "Online softmax: carry the max and the sum";
+ *   - grouped KV heads: "GPU and LLM" ch. 5, section "GQA";
+ *   - 16-token KV blocks behind a block table: "GPU and LLM" ch. 5, section
+ *     "PagedAttention (2)";
+ *   - FP8 KV storage with scaling factors: novita.ai blog "Revolutionizing LLM
+ *     inference: speculative decoding and low-precision quantization",
+ *     sections "Proprietary FP8 quantization scheme" and "KVCache quantization".
+ *
+ * General rules for every call:
+ *   - All tensor arguments are device pointers to dense row-major arrays that
+ *     the caller allocates and owns.  The library never allocates, frees or
+ *     synchronizes, keeps no state between calls and is safe to call from
+ *     several host threads.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *     Outputs are valid once that stream has been synchronized.
+ *   - Every argument check the host can make (NULL pointers, sizes, shapes,
+ *     alignment, support, workspace size) happens before anything is launched;
+ *     a failed check returns an error code, launches nothing and records a
+ *     message retrievable with sv_last_error() on the calling thread.
+ *   - Data on the device is not checked (it would need a synchronization).
+ *     The preconditions are stated per call; breaking them gives unspecified
+ *     output values but never an access outside the buffers described here.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_INVALID = 1,     /* a pointer, size, shape or alignment argument is invalid */
+  SV_ERR_WORKSPACE = 2,   /* the workspace is missing or smaller than required */
+  SV_ERR_UNSUPPORTED = 3, /* well formed, but not a supported configuration */
+  SV_ERR_LAUNCH = 4       /* the HIP runtime reported an error for a launch */
+} sv_status;
+
+typedef enum sv_kv_dtype {
+  SV_KV_BF16 = 0,         /* bfloat16 K and V */
+  SV_KV_FP8_E4M3 = 1      /* OCP e4m3 codes, one fp32 scale per (block, KV head) */
+} sv_kv_dtype;
+
+/* Shape and options of one spec_verify_attn call.  Sizes are element counts. */
+typedef struct sv_attn_params {
+  int32_t batch;              /* B >= 1 sequences */
+  int32_t draft_len;          /* D in [0, 63]; R = D + 1 query positions per sequence */
+  int32_t num_q_heads;        /* H_q >= 1 */
+  int32_t num_kv_heads;       /* H_kv >= 1, divides H_q; G = H_q / H_kv */
+  int32_t head_dim;           /* hd: 64 or 128 */
+  int32_t block_size;         /* tokens per KV block: must be 16 */
+  int32_t max_blocks_per_seq; /* columns of block_table, >= ceil(max_kv_len / 16) */
+  int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
+  int32_t max_kv_len;         /* upper bound on every kv_lens[b], >= R; sizes the
+                                 launch grid and the workspace on the host */
+  int32_t kv_dtype;           /* an sv_kv_dtype */
+  float sm_scale;             /* softmax scale applied to q.k, > 0 (usually 1/sqrt(hd)) */
+  int32_t split_tokens;       /* keys per split-K partition: 0 = chosen by the
+                                 library, else a positive multiple of 64 */
+} sv_attn_params;
+
+/*
+ * Bytes of device workspace spec_verify_attn needs for `p`.  May be 0.
+ * Returns SV_ERR_INVALID / SV_ERR_UNSUPPORTED for parameters spec_verify_attn
+ * would reject.
+ */
+sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes);
+
+/*
+ * Attention of the R = D + 1 newest positions of every sequence.
+ *
+ * For sequence b with L_b = kv_lens[b] keys (the context plus the R new
+ * positions, whose K and V are already in the cache), position i in 0..D,
+ * query head h and its KV head kvh = h / G:
+ *     s_t = sm_scale * q[b][i][h] . K_b[t][kvh]         for t = 0 .. L_b - R + i
+ *     out[b][i][h] = sum_t softmax(s)_t * V_b[t][kvh]
+ * computed with a running max and running sum over key tiles; key ranges of
+ * `split_tokens` keys are processed independently and merged with the same
+ * rescaling rule.  Accumulation is fp32; out is rounded to bf16 (nearest even).
+ *
+ *   q            [B][R][H_q][hd] bf16.                                16-byte aligned.
+ *   k_cache      bf16: [num_blocks][H_kv][hd/8][16][8]  (16-byte vectors of 8
+ *                      dims per token: element (blk, kvh, token slot s, dim d)
+ *                      is at ((blk*H_kv + kvh)*hd/8 + d/8)*128 + s*8 + d%8)
+ *                e4m3: [num_blocks][H_kv][hd/16][16][16] (uint8 codes; element
+ *                      at ((blk*H_kv + kvh)*hd/16 + d/16)*256 + s*16 + d%16).
+ *                                                                 16-byte aligned.
+ *   v_cache      [num_blocks][H_kv][hd][16]: element (blk, kvh, s, d) is at
+ *                ((blk*H_kv + kvh)*hd + d)*16 + s; bf16 or uint8 e4m3 codes.
+ *                                                                 16-byte aligned.
+ *   k_scale,     [num_blocks][H_kv] fp32: the value of an e4m3 code is
+ *   v_scale      decode(code) * scale[blk][kvh].  Required for e4m3, must be
+ *                NULL for bf16.
+ *   block_table  [B][max_blocks_per_seq] int32: token t of sequence b is in
+ *                physical block block_table[b][t / 16], slot t % 16.
+ *   kv_lens      [B] int32, L_b.
+ *   out          [B][R][H_q][hd] bf16, written.  16-byte aligned; must not
+ *                overlap any input.
+ *   workspace    device memory of at least spec_verify_attn_workspace_size()
+ *                bytes (may be NULL when that size is 0), 256-byte aligned;
+ *                contents on entry are ignored.
+ *
+ * Device preconditions: R <= kv_lens[b] <= max_kv_len; block_table[b][j] in
+ * [0, num_blocks) for j < ceil(kv_lens[b] / 16) (other entries are never read);
+ * K and V slots past kv_lens[b] may hold anything, NaN included.
+ */
+sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* kv_lens, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace spec_accept needs for (batch, draft_len, vocab). */
+sv_status spec_accept_workspace_size(int32_t batch, int32_t draft_len, int32_t vocab,
+                                     size_t* bytes);
+
+/*
+ * Greedy acceptance.
+ *
+ * For sequence b and row j in 0..D (row j is the target's prediction after
+ * input position j; row D is the bonus position):
+ *     target_tokens[b][j] = lowest v with logits[b][j][v] = max_v logits[b][j][v]
+ *                           (fp32 compares, so -0 == +0; all -inf -> 0)
+ *     n  = first j < D with draft[b][j] != target_tokens[b][j], else D
+ *     accept_len[b]  = n + 1                                  (1 .. 1 + D)
+ *     out_tokens[b]  = draft[b][0..n) , target_tokens[b][n] , -1 padding
+ *     kv_lens_out[b] = kv_lens_in[b] - (1 + D) + accept_len[b]
+ *
+ *   logits         [B][1+D][V] fp32; 16-byte aligned.  Finite or -inf (NaN
+ *                  gives unspecified tokens).
+ *   draft          [B][D] int32 (may be NULL when D = 0).  Ids outside [0, V)
+ *                  are allowed and never match.
+ *   target_tokens  [B][1+D] int32, written.
+ *   accept_len     [B] int32, written.
+ *   out_tokens     [B][1+D] int32, written.
+ *   kv_lens_in     [B] int32, read.
+ *   kv_lens_out    [B] int32, written; may be the same pointer as kv_lens_in
+ *                  (in-place commit).
+ *   workspace      at least spec_accept_workspace_size() bytes, 256-byte aligned.
+ */
+sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
+                      const int32_t* draft, int32_t* target_tokens, int32_t* accept_len,
+                      int32_t* out_tokens, const int32_t* kv_lens_in, int32_t* kv_lens_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* sv_status_string(sv_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sv_last_error(void);
+
+/* SV_ABI_VERSION of the built library. */
+int32_t sv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

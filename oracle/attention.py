@@ -52,27 +52,37 @@ def _decode(codes: np.ndarray) -> np.ndarray:
     raise TypeError(f"unsupported cache element type {codes.dtype}")
 
 
-def gather_kv(k_cache, v_cache, k_scale, v_scale, block_table, b, L):
+def gather_kv(k_cache, v_cache, k_scale, v_scale, block_table, b, L, kv_heads=None):
     """Logical K and V of sequence ``b`` for tokens 0..L-1, as fp64 [L][H_kv][hd].
 
-    Token t lives in physical block block_table[b][t // 16], slot t % 16.
+    Token t lives in physical block block_table[b][t // 16], slot t % 16.  With
+    ``kv_heads`` only those KV heads are decoded (the others are NaN).
     """
     nb = -(-int(L) // BLOCK)
     blocks = np.asarray(block_table[b, :nb], dtype=np.int64)
     if nb and (blocks < 0).any():
         raise ValueError("block table entry < 0 inside the sequence")
-    kb = k_cache[blocks]                              # [nb][H_kv][hd/X][16][X]
-    nbk, H_kv, nx, bs, X = kb.shape
-    k_tok = kb.transpose(0, 3, 1, 2, 4).reshape(nb * BLOCK, H_kv, nx * X)
-    vb = v_cache[blocks]                              # [nb][H_kv][hd][16]
-    v_tok = vb.transpose(0, 3, 1, 2).reshape(nb * BLOCK, H_kv, vb.shape[2])
-    K = _decode(k_tok[:L])
-    V = _decode(v_tok[:L])
+    H_kv = k_cache.shape[1]
+    heads = np.arange(H_kv) if kv_heads is None else np.asarray(list(kv_heads), dtype=np.int64)
+    kb = k_cache[blocks][:, heads]                    # [nb][h][hd/X][16][X]
+    _, nh, nx, bs, X = kb.shape
+    k_tok = kb.transpose(0, 3, 1, 2, 4).reshape(nb * BLOCK, nh, nx * X)
+    vb = v_cache[blocks][:, heads]                    # [nb][h][hd][16]
+    v_tok = vb.transpose(0, 3, 1, 2).reshape(nb * BLOCK, nh, vb.shape[2])
+    Kh = _decode(k_tok[:L])
+    Vh = _decode(v_tok[:L])
     if k_cache.dtype == np.uint8:
-        ks = np.repeat(np.asarray(k_scale, np.float64)[blocks], BLOCK, axis=0)[:L]  # [L][H_kv]
-        vs = np.repeat(np.asarray(v_scale, np.float64)[blocks], BLOCK, axis=0)[:L]
-        K = K * ks[:, :, None]
-        V = V * vs[:, :, None]
+        sel = np.ix_(blocks, heads)
+        ks = np.repeat(np.asarray(k_scale, np.float64)[sel], BLOCK, axis=0)[:L]  # [L][h]
+        vs = np.repeat(np.asarray(v_scale, np.float64)[sel], BLOCK, axis=0)[:L]
+        Kh = Kh * ks[:, :, None]
+        Vh = Vh * vs[:, :, None]
+    if kv_heads is None:
+        return Kh, Vh
+    K = np.full((int(L), H_kv, nx * X), np.nan)
+    V = np.full((int(L), H_kv, vb.shape[2]), np.nan)
+    K[:, heads] = Kh
+    V[:, heads] = Vh
     return K, V
 
 
@@ -94,15 +104,15 @@ def oracle_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, *,
     G = H_q // H_kv
     out = np.full((B, R, H_q, hd), np.nan)
     seqs = range(B) if seqs is None else seqs
-    kv_heads = range(H_kv) if kv_heads is None else kv_heads
     for b in seqs:
         L = int(kv_lens[b])
         if L < R:
             raise ValueError("kv_lens[b] must include the R new positions")
-        K, V = gather_kv(k_cache, v_cache, k_scale, v_scale, block_table, b, L)
+        K, V = gather_kv(k_cache, v_cache, k_scale, v_scale, block_table, b, L,
+                         None if kv_heads is None else list(kv_heads))
         Q = bf16_bits_to_f64(q[b])                     # [R][H_q][hd]
         vis = _visible(R, L)
-        for kvh in kv_heads:
+        for kvh in (range(H_kv) if kv_heads is None else kv_heads):
             for g in range(G):
                 h = kvh * G + g
                 s = sm_scale * (Q[:, h, :] @ K[:, kvh, :].T)      # [R][L]

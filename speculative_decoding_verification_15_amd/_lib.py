@@ -1,0 +1,155 @@
+"""ctypes binding of libspecverify.so.
+
+Argument marshalling only: tensors become device pointers, shapes become the
+C structs and integers the header declares, and a non-OK status becomes an
+SvError.  Every step of the verification path runs in the library's HIP
+kernels; nothing here computes.  Importing this module without a built library
+raises ImportError (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED, SV_ERR_LAUNCH = range(5)
+SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1
+
+# Every symbol include/spec_verify.h declares.
+EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_workspace_size",
+           "spec_accept", "sv_status_string", "sv_last_error", "sv_abi_version")
+
+
+class SvAttnParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("draft_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("split_tokens", ctypes.c_int32),
+    ]
+
+
+class SvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)} -- {message}")
+        self.status = status
+
+
+def _load():
+    # PyTorch ships its own HIP runtime (same soname as ROCm's).  Loading torch
+    # first makes the library bind to that runtime, so the process has exactly
+    # one HIP runtime and torch's device memory and streams are valid here.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m speculative_decoding_verification_15_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S, I32, U = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int
+    lib.spec_verify_attn_workspace_size.argtypes = [ctypes.POINTER(SvAttnParams), ctypes.POINTER(S)]
+    lib.spec_verify_attn_workspace_size.restype = U
+    lib.spec_verify_attn.argtypes = [ctypes.POINTER(SvAttnParams)] + [P] * 9 + [S, P]
+    lib.spec_verify_attn.restype = U
+    lib.spec_accept_workspace_size.argtypes = [I32, I32, I32, ctypes.POINTER(S)]
+    lib.spec_accept_workspace_size.restype = U
+    lib.spec_accept.argtypes = [I32, I32, I32] + [P] * 8 + [S, P]
+    lib.spec_accept.restype = U
+    lib.sv_status_string.argtypes = [U]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_last_error.argtypes = []
+    lib.sv_last_error.restype = ctypes.c_char_p
+    lib.sv_abi_version.argtypes = []
+    lib.sv_abi_version.restype = I32
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.sv_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib.sv_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(_lib.sv_abi_version())
+
+
+def _check(status: int):
+    if status != SV_OK:
+        raise SvError(status, last_error())
+
+
+def _ptr(t):
+    """Device address of a tensor (None -> NULL).  Integers pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_attn_params(*, batch, draft_len, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                     num_blocks, max_kv_len, kv_dtype=SV_KV_BF16, sm_scale=None, split_tokens=0,
+                     block_size=16) -> SvAttnParams:
+    if sm_scale is None:
+        sm_scale = head_dim ** -0.5
+    return SvAttnParams(batch, draft_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, max_kv_len, kv_dtype, sm_scale, split_tokens)
+
+
+def spec_verify_attn_workspace_size(params: SvAttnParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.spec_verify_attn_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return int(n.value)
+
+
+def spec_verify_attn(params: SvAttnParams, q, k_cache, v_cache, k_scale, v_scale, block_table,
+                     kv_lens, out, workspace=None, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(_lib.spec_verify_attn(ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(kv_lens),
+                                 _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def spec_accept_workspace_size(batch: int, draft_len: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.spec_accept_workspace_size(batch, draft_len, vocab, ctypes.byref(n)))
+    return int(n.value)
+
+
+def spec_accept(batch, draft_len, vocab, logits, draft, target_tokens, accept_len, out_tokens,
+                kv_lens_in, kv_lens_out, workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(_lib.spec_accept(batch, draft_len, vocab, _ptr(logits), _ptr(draft), _ptr(target_tokens),
+                            _ptr(accept_len), _ptr(out_tokens), _ptr(kv_lens_in), _ptr(kv_lens_out),
+                            _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -1,0 +1,194 @@
+// C ABI entry points (include/spec_verify.h): argument checks, workspace
+// sizing and dispatch to the gfx950 kernels.  Every check the host can make
+// runs before the first HIP call, so invalid calls return an error without
+// touching the device.
+#include "spec_verify.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sv_status fail(sv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxDraft = 63;
+constexpr int kMaxGridYZ = 65535;
+
+// Validates the shape in `p` and fills `plan`.  No pointer is looked at.
+sv_status make_attn_plan(const sv_attn_params* p, sv::AttnPlan& plan) {
+  if (!p) return fail(SV_ERR_INVALID, "params is NULL");
+  if (p->batch < 1) return fail(SV_ERR_INVALID, "batch must be >= 1 (got %d)", p->batch);
+  if (p->draft_len < 0 || p->draft_len > kMaxDraft)
+    return fail(SV_ERR_INVALID, "draft_len must be in [0, %d] (got %d)", kMaxDraft, p->draft_len);
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return fail(SV_ERR_INVALID, "head counts must be >= 1 (H_q=%d, H_kv=%d)", p->num_q_heads,
+                p->num_kv_heads);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(SV_ERR_INVALID, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->block_size != 16)
+    return fail(SV_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", p->block_size);
+  if (p->kv_dtype != SV_KV_BF16 && p->kv_dtype != SV_KV_FP8_E4M3)
+    return fail(SV_ERR_INVALID, "unknown kv_dtype %d", p->kv_dtype);
+  if (!(p->sm_scale > 0.f) || !std::isfinite(p->sm_scale))
+    return fail(SV_ERR_INVALID, "sm_scale must be finite and > 0");
+  const int R = p->draft_len + 1;
+  if (p->max_kv_len < R)
+    return fail(SV_ERR_INVALID, "max_kv_len (%d) must be >= 1 + draft_len (%d)", p->max_kv_len, R);
+  if (p->num_blocks < 1) return fail(SV_ERR_INVALID, "num_blocks must be >= 1");
+  const long long need_blocks = (p->max_kv_len + 15LL) / 16;
+  if (p->max_blocks_per_seq < need_blocks)
+    return fail(SV_ERR_INVALID, "max_blocks_per_seq (%d) < ceil(max_kv_len / 16) (%lld)",
+                p->max_blocks_per_seq, need_blocks);
+  if (p->split_tokens < 0 || p->split_tokens % sv::kAttnTile != 0)
+    return fail(SV_ERR_INVALID, "split_tokens must be 0 or a positive multiple of %d (got %d)",
+                sv::kAttnTile, p->split_tokens);
+  if (p->batch > kMaxGridYZ) return fail(SV_ERR_UNSUPPORTED, "batch > %d", kMaxGridYZ);
+  // index arithmetic inside the kernels uses 32-bit row counts
+  const long long q_elems = (long long)p->batch * R * p->num_q_heads * p->head_dim;
+  if (q_elems >= (1LL << 31)) return fail(SV_ERR_UNSUPPORTED, "q/out larger than 2^31 elements");
+
+  plan = sv::AttnPlan{};
+  plan.B = p->batch;
+  plan.R = R;
+  plan.H_q = p->num_q_heads;
+  plan.H_kv = p->num_kv_heads;
+  plan.hd = p->head_dim;
+  plan.max_blocks = p->max_blocks_per_seq;
+  plan.num_blocks = p->num_blocks;
+  plan.max_kv_len = p->max_kv_len;
+  plan.fp8 = p->kv_dtype == SV_KV_FP8_E4M3;
+  plan.sm_scale = p->sm_scale;
+  sv::plan_attention(plan, p->split_tokens);
+  if ((long long)plan.H_kv * plan.m_tiles > kMaxGridYZ)
+    return fail(SV_ERR_UNSUPPORTED, "num_kv_heads * row tiles exceeds the grid limit");
+  const long long ws_rows = (long long)plan.B * plan.H_kv * plan.s_max * plan.M;
+  if (ws_rows >= (1LL << 31)) return fail(SV_ERR_UNSUPPORTED, "split workspace too large");
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes) {
+  if (!bytes) return fail(SV_ERR_INVALID, "bytes is NULL");
+  sv::AttnPlan plan;
+  sv_status s = make_attn_plan(p, plan);
+  if (s != SV_OK) return s;
+  *bytes = plan.ws_bytes;
+  return SV_OK;
+}
+
+sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* kv_lens, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  sv::AttnPlan plan;
+  sv_status s = make_attn_plan(p, plan);
+  if (s != SV_OK) return s;
+  if (!q || !k_cache || !v_cache || !block_table || !kv_lens || !out)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(SV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(kv_lens, 4))
+    return fail(SV_ERR_INVALID, "block_table and kv_lens must be 4-byte aligned");
+  if (plan.fp8) {
+    if (!k_scale || !v_scale) return fail(SV_ERR_INVALID, "e4m3 caches need k_scale and v_scale");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4))
+      return fail(SV_ERR_INVALID, "k_scale and v_scale must be 4-byte aligned");
+  } else if (k_scale || v_scale) {
+    return fail(SV_ERR_INVALID, "k_scale and v_scale must be NULL for bf16 caches");
+  }
+  if (plan.ws_bytes > 0) {
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(SV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                  plan.ws_bytes);
+    if (!aligned(workspace, 256)) return fail(SV_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
+  sv::AttnPtrs ptrs{q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, out, workspace};
+  hipError_t e = sv::launch_attention(plan, ptrs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+static sv_status check_accept_shape(int32_t batch, int32_t draft_len, int32_t vocab) {
+  if (batch < 1) return fail(SV_ERR_INVALID, "batch must be >= 1 (got %d)", batch);
+  if (draft_len < 0 || draft_len > kMaxDraft)
+    return fail(SV_ERR_INVALID, "draft_len must be in [0, %d] (got %d)", kMaxDraft, draft_len);
+  if (vocab < 1) return fail(SV_ERR_INVALID, "vocab must be >= 1 (got %d)", vocab);
+  const long long rows = (long long)batch * (draft_len + 1);
+  if (rows > kMaxGridYZ) return fail(SV_ERR_UNSUPPORTED, "batch * (1 + draft_len) > %d", kMaxGridYZ);
+  if (batch > 2147483647 / 64) return fail(SV_ERR_UNSUPPORTED, "batch too large");
+  return SV_OK;
+}
+
+sv_status spec_accept_workspace_size(int32_t batch, int32_t draft_len, int32_t vocab,
+                                     size_t* bytes) {
+  if (!bytes) return fail(SV_ERR_INVALID, "bytes is NULL");
+  sv_status s = check_accept_shape(batch, draft_len, vocab);
+  if (s != SV_OK) return s;
+  *bytes = sv::accept_workspace_bytes(batch, draft_len, vocab);
+  return SV_OK;
+}
+
+sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
+                      const int32_t* draft, int32_t* target_tokens, int32_t* accept_len,
+                      int32_t* out_tokens, const int32_t* kv_lens_in, int32_t* kv_lens_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status s = check_accept_shape(batch, draft_len, vocab);
+  if (s != SV_OK) return s;
+  if (!logits || !target_tokens || !accept_len || !out_tokens || !kv_lens_in || !kv_lens_out)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (draft_len > 0 && !draft) return fail(SV_ERR_INVALID, "draft is NULL with draft_len > 0");
+  if (!aligned(logits, 16)) return fail(SV_ERR_INVALID, "logits must be 16-byte aligned");
+  if (!aligned(target_tokens, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
+      !aligned(kv_lens_in, 4) || !aligned(kv_lens_out, 4) || (draft && !aligned(draft, 4)))
+    return fail(SV_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  const size_t need = sv::accept_workspace_bytes(batch, draft_len, vocab);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(SV_ERR_INVALID, "workspace must be 256-byte aligned");
+  hipError_t e = sv::launch_accept(batch, draft_len, vocab, logits, draft, target_tokens,
+                                   accept_len, out_tokens, kv_lens_in, kv_lens_out, workspace,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_INVALID: return "SV_ERR_INVALID: invalid argument";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace missing or too small";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED: configuration not supported";
+    case SV_ERR_LAUNCH: return "SV_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown sv_status";
+}
+
+const char* sv_last_error(void) { return g_err; }
+
+int32_t sv_abi_version(void) { return SV_ABI_VERSION; }
+
+}  // extern "C"

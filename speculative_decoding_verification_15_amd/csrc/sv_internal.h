@@ -1,0 +1,57 @@
+// Host-side interface between the C ABI layer (sv_api.cpp) and the kernel
+// launchers (sv_attn.hip, sv_accept.hip).  Arguments reaching these launchers
+// have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+// Keys per attention tile iteration; split boundaries are multiples of it.
+constexpr int kAttnTile = 64;
+// Query rows per wave (one 32-wide MFMA operand).
+constexpr int kRowsPerWave = 32;
+
+struct AttnPlan {
+  int B, R, H_q, H_kv, G, M, hd;
+  int max_blocks, num_blocks, max_kv_len;
+  bool fp8;
+  float sm_scale;
+  int split_tokens;  // keys per split (multiple of kAttnTile)
+  int s_max;         // ceil(max_kv_len / split_tokens)
+  int waves;         // waves per workgroup (each owns 32 query rows)
+  int m_tiles;       // ceil(M / (32 * waves))
+  size_t ws_o_bytes, ws_ml_offset, ws_bytes;
+};
+
+struct AttnPtrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* kv_lens;
+  void* out;
+  void* ws;
+};
+
+// Fills split/grid/workspace fields of `plan` from its shape fields.
+void plan_attention(AttnPlan& plan, int split_tokens_request);
+hipError_t launch_attention(const AttnPlan& plan, const AttnPtrs& ptrs, hipStream_t stream);
+
+constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxChunk = kArgmaxThreads * 4 * 8;  // logits per workgroup
+
+inline int argmax_chunks(int vocab) { return (vocab + kArgmaxChunk - 1) / kArgmaxChunk; }
+inline size_t accept_workspace_bytes(int B, int D, int V) {
+  return (size_t)B * (size_t)(D + 1) * (size_t)argmax_chunks(V) * 8u;
+}
+
+hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t* draft,
+                         int32_t* target, int32_t* accept_len, int32_t* out_tokens,
+                         const int32_t* kv_in, int32_t* kv_out, void* ws, hipStream_t stream);
+
+}  // namespace sv

@@ -1,3 +1,4 @@
+import importlib.util
 import os
 import sys
 
@@ -7,10 +8,24 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PKG_DIR = os.path.join(ROOT, "speculative_decoding_verification_15_amd")
+LIB = os.path.join(PKG_DIR, "libspecverify.so")
+
+
+def _build_if_missing():
+    """Build the library only when nothing is built (build() always rebuilds)."""
+    if os.path.exists(LIB):
+        return
+    spec = importlib.util.spec_from_file_location("_sv_build", os.path.join(PKG_DIR, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.build()
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+    _build_if_missing()
 
 
 @pytest.fixture(scope="session")

@@ -1,0 +1,108 @@
+"""GPU parity of spec_verify_attn against the fp64 oracle.
+
+Tolerance (per element, on the bf16 output decoded to fp64): max-abs <= 1e-2
+and mean-abs <= 1e-3 against the oracle for N(0,1) inputs.
+
+  * reduced shapes, every output element, with the split size forced to one
+    tile, two tiles, the automatic choice, and one split for everything (the
+    no-merge path);
+  * the full verification-step shapes (8B-like, 70B-like ragged, fp8 long
+    context, the tile-boundary sweep), on sampled (sequence, KV head) pairs the
+    oracle computes one by one, plus "every row finite" over all outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import oracle_attn
+from tests.gpu_util import (MAX_ABS_TOL, MEAN_ABS_TOL, DeviceAttn, attn_errors, note,
+                            run_attention)
+from workloads import (EDGE, FP8_LONG, LLAMA3_8B, LLAMA31_70B, MINI, SWEEP_D, TINY,
+                       make_attn_inputs, tile_sweep)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [TINY] + list(MINI.values()) + list(EDGE.values())
+
+
+def oracle_for(inp, **kw):
+    w = inp.w
+    return oracle_attn(inp.q, inp.k_cache, inp.v_cache, inp.k_scale, inp.v_scale,
+                       inp.block_table, inp.kv_lens, D=w.D, H_kv=w.H_kv, sm_scale=w.sm_scale,
+                       **kw)
+
+
+def check(gpu, ref, label):
+    mx, mean, rel = attn_errors(gpu, ref)
+    note(f"  {label}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_l2={rel:.3e}")
+    assert mx <= MAX_ABS_TOL, (label, mx)
+    assert mean <= MEAN_ABS_TOL, (label, mean)
+    return rel
+
+
+@pytest.mark.parametrize("split", [0, 64, 128, 1 << 20])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_attention_small_all_elements(w, split):
+    inp = make_attn_inputs(w)
+    ref = oracle_for(inp)
+    gpu = run_attention(inp, split_tokens=split)
+    assert np.isfinite(gpu).all()
+    rel = check(gpu, ref, f"{w.name}/split={split}")
+    assert rel < 1e-2
+
+
+def _samples(inp, n_rand=2, seed=0):
+    w = inp.w
+    L = inp.kv_lens
+    rng = np.random.default_rng(seed)
+    bs = {int(np.argmin(L)), int(np.argmax(L))} | set(rng.integers(0, w.B, n_rand).tolist())
+    hs = {0, w.H_kv - 1}
+    return sorted(bs), sorted(hs)
+
+
+def _full_size(w, split=0):
+    note(f"[gen] {w.name}")
+    inp = make_attn_inputs(w)
+    gpu = run_attention(inp, split_tokens=split)
+    assert np.isfinite(gpu).all(), "a row is not finite"
+    seqs, heads = _samples(inp)
+    note(f"[oracle] {w.name} seqs={seqs} kv_heads={heads}")
+    ref = oracle_for(inp, seqs=seqs, kv_heads=heads)
+    check(gpu, ref, w.name)
+
+
+@pytest.mark.parametrize("w", [LLAMA3_8B, LLAMA31_70B, FP8_LONG], ids=lambda w: w.name)
+def test_attention_full_size_sampled(w):
+    _full_size(w)
+
+
+@pytest.mark.parametrize("mqa", [False, True], ids=["gqa8", "mqa"])
+@pytest.mark.parametrize("D", SWEEP_D)
+def test_attention_tile_sweep_sampled(D, mqa):
+    _full_size(tile_sweep(D, mqa))
+
+
+def test_tiny_contiguous_exact_shape():
+    inp = make_attn_inputs(TINY)
+    assert inp.kv_lens.tolist() == [260] and (inp.block_table[0, :17] == np.arange(17)).all()
+    check(run_attention(inp), oracle_for(inp), "tiny")
+
+
+def test_repeatable_and_stream_independent():
+    inp = make_attn_inputs(MINI["mini_gqa8_d15"])
+    d = DeviceAttn(inp)
+    a = d.run(64).cpu().numpy()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = d.run(64, stream=s).cpu().numpy()
+    c = d.run(64).cpu().numpy()
+    assert (a == b).all() and (a == c).all()
+
+
+def test_split_results_agree_closely():
+    inp = make_attn_inputs(MINI["mini_gqa4_d7"])
+    d = DeviceAttn(inp)
+    one = DeviceAttn.to_f64(d.run(1 << 20))
+    many = DeviceAttn.to_f64(d.run(64))
+    # different merge orders round differently, but only at bf16 resolution
+    assert np.abs(one - many).max() <= 2 * 2.0 ** -8 * np.abs(one).max()

@@ -40,7 +40,7 @@ def test_wrong_kv_head_is_caught(monkeypatch):
 
 
 def test_transposed_v_block_is_caught(monkeypatch):
-    def wrong_gather(k_cache, v_cache, k_scale, v_scale, block_table, b, L):
+    def wrong_gather(k_cache, v_cache, k_scale, v_scale, block_table, b, L, kv_heads=None):
         nb = -(-int(L) // 16)
         blocks = np.asarray(block_table[b, :nb], dtype=np.int64)
         kb = k_cache[blocks]
