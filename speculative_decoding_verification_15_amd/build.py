@@ -18,8 +18,11 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 SOURCES = ("sv_api.cpp", "sv_attn.hip", "sv_accept.hip")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 VALU forms are disabled for all device code.  MFMA accumulators
+# are kept in VGPRs (the softmax reads the score accumulators and rescales the
+# output accumulators with VALU ops, which cannot take AGPR operands).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 

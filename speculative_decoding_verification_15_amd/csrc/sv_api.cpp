@@ -59,7 +59,6 @@ sv_status make_attn_plan(const sv_attn_params* p, sv::AttnPlan& plan) {
   if (p->split_tokens < 0 || p->split_tokens % sv::kAttnTile != 0)
     return fail(SV_ERR_INVALID, "split_tokens must be 0 or a positive multiple of %d (got %d)",
                 sv::kAttnTile, p->split_tokens);
-  if (p->batch > kMaxGridYZ) return fail(SV_ERR_UNSUPPORTED, "batch > %d", kMaxGridYZ);
   // index arithmetic inside the kernels uses 32-bit row counts
   const long long q_elems = (long long)p->batch * R * p->num_q_heads * p->head_dim;
   if (q_elems >= (1LL << 31)) return fail(SV_ERR_UNSUPPORTED, "q/out larger than 2^31 elements");
@@ -76,8 +75,9 @@ sv_status make_attn_plan(const sv_attn_params* p, sv::AttnPlan& plan) {
   plan.fp8 = p->kv_dtype == SV_KV_FP8_E4M3;
   plan.sm_scale = p->sm_scale;
   sv::plan_attention(plan, p->split_tokens);
-  if ((long long)plan.H_kv * plan.m_tiles > kMaxGridYZ)
-    return fail(SV_ERR_UNSUPPORTED, "num_kv_heads * row tiles exceeds the grid limit");
+  const long long units = (long long)plan.s_max * plan.B * plan.H_kv;
+  if (((units + 7) / 8) * 8 * plan.m_tiles >= (1LL << 31))
+    return fail(SV_ERR_UNSUPPORTED, "too many workgroups for one launch");
   const long long ws_rows = (long long)plan.B * plan.H_kv * plan.s_max * plan.M;
   if (ws_rows >= (1LL << 31)) return fail(SV_ERR_UNSUPPORTED, "split workspace too large");
   return SV_OK;

@@ -56,9 +56,9 @@ struct AttnArgs {
   uint16_t* out;
   float* ws_o;    // [B][H_kv][s_max][M][hd] unnormalised O of each split
   f32x2* ws_ml;   // [B][H_kv][s_max][M] (m, l) of each split, log2 domain
-  int R, H_q, H_kv, G, M;
+  int B, R, H_q, H_kv, G, M;
   int max_blocks, num_blocks, max_kv_len;
-  int split_tokens, s_max;
+  int split_tokens, s_max, m_tiles;
   float c;        // sm_scale * log2(e)
 };
 
@@ -105,6 +105,34 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int b) {
   return min(max(a.kv_lens[b], 0), a.max_kv_len);
 }
 
+// Work item of this workgroup.  The grid is one-dimensional and the hardware
+// hands consecutive workgroup ids to the 8 XCDs in turn, so the id is decoded
+// as (xcd = id % 8, k = id / 8): unit u = (k / m_tiles) * 8 + xcd, row tile
+// mt = k % m_tiles.  All row tiles of a unit (same sequence, KV head and
+// split, hence the same K/V) run on one XCD and share its L2, and units --
+// ordered split-major, (sequence, KV head) minor -- are dealt round-robin over
+// the XCDs, so short sequences' missing splits do not pile up on one XCD.
+struct Work {
+  int split, kvh, mt, b;
+  bool valid;
+};
+
+__device__ __forceinline__ Work decode_work(const AttnArgs& a, int m_tiles) {
+  constexpr int kXcds = 8;
+  const int id = blockIdx.x;
+  const int k = id / kXcds;
+  const int unit = (k / m_tiles) * kXcds + id % kXcds;
+  const int bk_units = a.B * a.H_kv;
+  Work w;
+  w.mt = k % m_tiles;
+  w.split = unit / bk_units;
+  const int bk = unit % bk_units;
+  w.b = bk / a.H_kv;
+  w.kvh = bk % a.H_kv;
+  w.valid = w.split < a.s_max;
+  return w;
+}
+
 // Physical block of logical block j of a sequence with n_blk blocks, clamped so
 // that a bad table entry or a block past the sequence never leaves the cache.
 __device__ __forceinline__ size_t phys_block(const AttnArgs& a, const int32_t* tbl, int j,
@@ -128,49 +156,73 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, const RowCtx& r, bf16x
 }
 
 // Online-softmax update for one 64-key tile whose raw scores q.k are in x
-// (two 32-key sub-blocks).  cs[sb][half] scales the scores of the 16-key block
-// `half` of sub-block sb into the log2 domain.  On return x holds the
-// probabilities exp2(x - m_new), o has been rescaled, and m_run / l_run updated.
-template <int DB>
-__device__ __forceinline__ void softmax_tile(f32x16 (&x)[2], const float (&cs)[2][2],
+// (two 32-key sub-blocks).  cs[sb][half] > 0 scales the scores of 16-key block
+// `half` of sub-block sb into the log2 domain.
+//
+// The reference m_ref against which exponentials are taken follows the running
+// max lazily: it moves (and O, l are rescaled by 2^(m_ref - m_new)) only when
+// the tile max exceeds it by more than kLazyRescale, so probabilities stay
+// below 2^kLazyRescale.  O / l is the same for any reference, so the result is
+// unchanged; it only saves the O rescale on the many tiles whose max grows a
+// little.  MASKED tiles apply the causal limit (key <= P + pos) and drop dead
+// sub-blocks; unmasked tiles have every key live and visible to every row.
+// On return x holds the probabilities.
+constexpr float kLazyRescale = 8.f;
+
+template <bool MASKED>
+__device__ __forceinline__ bool softmax_core(f32x16 (&x)[2], const float (&cs)[2][2],
                                              const bool (&live)[2], int kt, const RowCtx& r,
-                                             float& m_run, float& l_run, f32x16 (&o)[DB]) {
+                                             float& m_ref, float& l_run, float& alpha) {
   float tmax = -INFINITY;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const int t0 = kt + 32 * sb;
-    const bool need_mask = t0 + 31 > r.P;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float s = x[sb][v] * (v < 8 ? cs[sb][0] : cs[sb][1]);
-      if (need_mask) {
-        const int key = t0 + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3));
-        if (key > r.vis_last) s = -INFINITY;
+    for (int half = 0; half < 2; ++half) {
+      float hm = -INFINITY;
+#pragma unroll
+      for (int v = 8 * half; v < 8 * half + 8; ++v) {
+        if constexpr (MASKED) {
+          const int key = kt + 32 * sb + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3));
+          if (!live[sb] || key > r.vis_last) x[sb][v] = -INFINITY;
+        }
+        hm = fmaxf(hm, x[sb][v]);
       }
-      if (!live[sb]) s = -INFINITY;
-      x[sb][v] = s;
-      tmax = fmaxf(tmax, s);
+      tmax = fmaxf(tmax, hm * cs[sb][half]);
     }
   }
   tmax = halves_max(tmax);
-  const float m_new = fmaxf(m_run, tmax);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(m_run - m_use);
+  bool move = false;
+  alpha = 1.f;
+  if (m_ref == -INFINITY) {
+    m_ref = tmax;                  // first visible keys of this row: O and l are still 0
+  } else if (tmax > m_ref + kLazyRescale) {
+    alpha = fast_exp2(m_ref - tmax);
+    m_ref = tmax;
+    move = true;
+  }
+  const float m_neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
   float psum = 0.f;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float p = fast_exp2(x[sb][v] - m_use);
+      const float p = fast_exp2(__builtin_fmaf(x[sb][v], cs[sb][v >> 3], m_neg));
       x[sb][v] = p;
       psum += p;
     }
   l_run = l_run * alpha + psum;
-  if (__ballot(alpha != 1.f)) {
+  return __ballot(move) != 0;
+}
+
+// Online-softmax update plus the O rescale in place (used by the direct kernel).
+template <int DB, bool MASKED>
+__device__ __forceinline__ void softmax_tile(f32x16 (&x)[2], const float (&cs)[2][2],
+                                             const bool (&live)[2], int kt, const RowCtx& r,
+                                             float& m_ref, float& l_run, f32x16 (&o)[DB]) {
+  float alpha;
+  softmax_core<MASKED>(x, cs, live, kt, r, m_ref, l_run, alpha);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-  }
-  m_run = m_new;
+  for (int db = 0; db < DB; ++db) o[db] *= alpha;
 }
 
 // P^T operand for PV step (sub-block sb, 16-key block kk): the 8 probabilities
@@ -228,10 +280,14 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const RowCtx& r,
 //      block reads position i & 15 of block i / 16 -- eight consecutive lanes
 //      read 128 contiguous bytes.
 //   V: 4 blocks x [hd dims][2 halves] x 16 B.  Half position hs of dim d holds
-//      token slots 8h .. 8h + 7 with h = hs ^ ((d >> 2) & 1), which spreads
-//      eight consecutive dims over all banks.
+//      token slots 8h .. 8h + 7 with h = hs ^ vhalf_swz(d), which spreads eight
+//      (and sixteen) consecutive dims over distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kLdsThreads = 256;
+#ifndef SV_RING_STAGES
+#define SV_RING_STAGES 2
+#define SV_RING_WPE 2
+#endif
 
 template <int HD>
 struct LdsTile {
@@ -241,7 +297,8 @@ struct LdsTile {
 };
 
 __device__ __forceinline__ int swap23(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
-__device__ __forceinline__ int vhalf_swz(int d) { return (d >> 2) & 1; }
+// Eight consecutive dims (and sixteen) land on distinct 16-byte bank groups.
+__device__ __forceinline__ int vhalf_swz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 
 // Zero the bf16 elements of an 8-slot V vector whose keys are >= L.
 __device__ __forceinline__ u32x4 zero_tail(u32x4 v, int key0, int L) {
@@ -259,11 +316,54 @@ __device__ __forceinline__ u32x4 bf16x8_bits(bf16x8 x) { return __builtin_bit_ca
 
 template <int HD, bool FP8>
 struct Stager {
-  // bf16: one 16-byte vector per (u, thread); e4m3: one 16-byte vector of codes
-  static constexpr int kGlobalVec = FP8 ? (2 * 4 * HD) : (2 * 4 * 2 * HD);   // per tile
-  static constexpr int kPerThread = kGlobalVec / kLdsThreads;
+  // 16-byte global vectors of one tile: bf16 K and V blocks, or e4m3 codes
+  static constexpr int kGlobBlk = FP8 ? HD : 2 * HD;         // vectors per cache block
+  static constexpr int kPerThread = 8 * kGlobBlk / kLdsThreads;
+  static constexpr int kBlkStep = kLdsThreads / kGlobBlk;    // blocks covered per u step
   u32x4 raw[kPerThread];
 };
+
+// One 64-key tile: S^T = K . Q^T on the LDS image, online-softmax update, and
+// O^T += V^T . P^T.
+template <int HD, bool FP8, bool MASKED>
+__device__ __forceinline__ void lds_tile(const AttnArgs& a, const RowCtx& r, const uint8_t* stage,
+                                         int k_lds, int v_lds, const bf16x8 (&qop)[HD / 16],
+                                         const float (&cs)[2][2], const float (&vs)[4], int kt,
+                                         float& m_ref, float& l_run, f32x16 (&o)[HD / 32]) {
+  constexpr int KS = HD / 16;
+  constexpr int DB = HD / 32;
+  constexpr int BLK = LdsTile<HD>::kBlk;
+  f32x16 x[2];
+  bool live[2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    live[sb] = MASKED ? (kt + 32 * sb < r.k_end) : true;
+    x[sb] = f32x16{};
+    if (!live[sb]) continue;
+    const uint8_t* kb = stage + k_lds + 2 * sb * BLK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + ks * 512);
+      x[sb] = mfma32x32x16(kop, qop[ks], x[sb]);
+    }
+  }
+  softmax_tile<DB, MASKED>(x, cs, live, kt, r, m_ref, l_run, o);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    if (!live[sb]) continue;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (MASKED && kt + 32 * sb + 16 * kk >= r.k_end) continue;
+      const bf16x8 pop = p_operand(x[sb], kk, FP8 ? vs[2 * sb + kk] : 1.f);
+      const uint8_t* vb = stage + v_lds + (4 + 2 * sb + kk) * BLK;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
+        o[db] = mfma32x32x16(vop, pop, o[db]);
+      }
+    }
+  }
+}
 
 template <int HD, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
@@ -273,17 +373,15 @@ void sv_attn_partial_lds(AttnArgs a) {
   constexpr int DB = HD / 32;
   using T = LdsTile<HD>;
   using S = Stager<HD, FP8>;
-  constexpr int kGlobBlk = FP8 ? HD : 2 * HD;      // 16-byte vectors per cache block
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::kStage];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y % a.H_kv;
-  const int mt = blockIdx.y / a.H_kv;
-  const int b = blockIdx.z;
+  const Work wk = decode_work(a, a.m_tiles);
+  if (!wk.valid) return;
+  const int split = wk.split, kvh = wk.kvh, mt = wk.mt, b = wk.b;
   const int L = clamp_len(a, b);
   if (split * a.split_tokens >= L) return;           // whole workgroup: no barrier yet
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int m0 = (mt * 4 + wave) * kRowsPerWave;
   const bool active = m0 < a.M;                       // inactive waves still load
@@ -295,72 +393,64 @@ void sv_attn_partial_lds(AttnArgs a) {
   const int32_t* tbl = a.block_table + (size_t)b * a.max_blocks;
   const int n_blk = (L + 15) / 16;
   const int ntiles = (r.k_end - r.k_begin + kAttnTile - 1) / kAttnTile;
-  const size_t kv_stride = (size_t)a.H_kv * (FP8 ? HD * 16 : HD * 32);   // bytes per physical block
+  const size_t blk_stride = (size_t)a.H_kv * (FP8 ? HD * 16 : HD * 32);   // bytes per physical block
   const size_t head_off = (size_t)kvh * (FP8 ? HD * 16 : HD * 32);
 
+  // Per-thread, loop-invariant parts of the tile copy.  Thread tid moves
+  // vector p of cache block bk(u) = u * kBlkStep + wave / (kGlobBlk / 64).
+  const int p = tid % S::kGlobBlk;
+  const int bk_wave = wave / (S::kGlobBlk / kWave);
+  int g_off_k, g_off_v;      // byte offsets inside a global (block, head) chunk
+  int l_off_k0, l_off_k1, l_off_v0, l_off_v1;   // byte offsets inside an LDS block image
+  if constexpr (!FP8) {
+    g_off_k = ((p >> 4) * 16 + swap23(p & 15)) * 16;
+    g_off_v = ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16;
+    l_off_k0 = l_off_v0 = p * 16;
+    l_off_k1 = l_off_v1 = 0;
+  } else {
+    g_off_k = g_off_v = p * 16;                     // K: (vector p/16, slot p%16); V: dim p
+    l_off_k0 = ((2 * (p >> 4)) * 16 + swap23(p & 15)) * 16;
+    l_off_k1 = l_off_k0 + 256;
+    l_off_v0 = (2 * p + vhalf_swz(p)) * 16;
+    l_off_v1 = (2 * p + (1 ^ vhalf_swz(p))) * 16;
+  }
+  // MFMA operand reads inside a stage.
+  const int k_lds = (r.ql >> 4) * T::kBlk + (r.ql & 15) * 16 + r.hh * 256;
+  const int v_lds = (2 * r.ql + (r.hh ^ vhalf_swz(r.ql))) * 16;
+
   S st;
-  // Fetch tile `t` (cache blocks 4 * (k_begin/16 + 4t) ...) into registers.
   auto fetch = [&](int t) {
     const int lb0 = r.k_begin / 16 + 4 * t;
 #pragma unroll
     for (int u = 0; u < S::kPerThread; ++u) {
-      const int qv = tid + kLdsThreads * u;
-      const int bk = qv / kGlobBlk;                  // 0..7: K blocks 0..3, V blocks 0..3
-      const int p = qv % kGlobBlk;
-      const int blk = bk & 3;
-      const size_t pb = phys_block(a, tbl, lb0 + blk, n_blk);
-      const uint8_t* base = (bk < 4 ? a.k : a.v) + pb * kv_stride + head_off;
-      int off;
-      if constexpr (!FP8) {
-        off = bk < 4 ? ((p >> 4) * 16 + swap23(p & 15)) * 16
-                     : ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16;
-      } else {
-        off = p * 16;   // K: (vector c, slot) ; V: dim d -- both 16 codes
-      }
-      st.raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+      const int bk = u * S::kBlkStep + bk_wave;                // wave-uniform
+      const uint8_t* base = (bk < 4 ? a.k : a.v) + phys_block(a, tbl, lb0 + (bk & 3), n_blk) * blk_stride + head_off;
+      st.raw[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(base + (bk < 4 ? g_off_k : g_off_v)));
     }
   };
-  // Write the fetched tile `t` into LDS stage `stage` (e4m3 decoded to bf16,
-  // V slots at or past L zeroed).
   auto commit = [&](int t, int stage) {
     uint8_t* sbase = smem + stage * T::kStage;
     const int key_tile = r.k_begin + kAttnTile * t;
     const bool tail = key_tile + kAttnTile > L;
 #pragma unroll
     for (int u = 0; u < S::kPerThread; ++u) {
-      const int qv = tid + kLdsThreads * u;
-      const int bk = qv / kGlobBlk;
-      const int p = qv % kGlobBlk;
-      const int blk = bk & 3;
+      const int bk = u * S::kBlkStep + bk_wave;
       uint8_t* dst = sbase + bk * T::kBlk;
+      const int key_blk = key_tile + 16 * (bk & 3);
       if constexpr (!FP8) {
         u32x4 v = st.raw[u];
-        if (bk >= 4 && tail) {
-          const int d = p >> 1;
-          const int h = (p & 1) ^ vhalf_swz(d);
-          v = zero_tail(v, key_tile + 16 * blk + 8 * h, L);
-        }
-        *reinterpret_cast<u32x4*>(dst + p * 16) = v;
+        if (bk >= 4 && tail) v = zero_tail(v, key_blk + 8 * ((p & 1) ^ vhalf_swz(p >> 1)), L);
+        *reinterpret_cast<u32x4*>(dst + l_off_k0) = v;
       } else {
-        const bf16x8 lo = e4m3x8_to_bf16(st.raw[u][0], st.raw[u][1]);
-        const bf16x8 hi = e4m3x8_to_bf16(st.raw[u][2], st.raw[u][3]);
+        const u32x4 lo = bf16x8_bits(e4m3x8_to_bf16(st.raw[u][0], st.raw[u][1]));
+        const u32x4 hi = bf16x8_bits(e4m3x8_to_bf16(st.raw[u][2], st.raw[u][3]));
         if (bk < 4) {
-          // codes of 16 dims (vector c8 = p / 16) of slot p % 16
-          const int c8 = p >> 4;
-          const int s = swap23(p & 15);
-          *reinterpret_cast<u32x4*>(dst + ((2 * c8) * 16 + s) * 16) = bf16x8_bits(lo);
-          *reinterpret_cast<u32x4*>(dst + ((2 * c8 + 1) * 16 + s) * 16) = bf16x8_bits(hi);
+          *reinterpret_cast<u32x4*>(dst + l_off_k0) = lo;
+          *reinterpret_cast<u32x4*>(dst + l_off_k1) = hi;
         } else {
-          // codes of 16 slots of dim d = p
-          const int d = p;
-          u32x4 v0 = bf16x8_bits(lo), v1 = bf16x8_bits(hi);
-          if (tail) {
-            v0 = zero_tail(v0, key_tile + 16 * blk, L);
-            v1 = zero_tail(v1, key_tile + 16 * blk + 8, L);
-          }
-          const int sw = vhalf_swz(d);
-          *reinterpret_cast<u32x4*>(dst + (2 * d + sw) * 16) = v0;
-          *reinterpret_cast<u32x4*>(dst + (2 * d + (1 ^ sw)) * 16) = v1;
+          *reinterpret_cast<u32x4*>(dst + l_off_v0) = tail ? zero_tail(lo, key_blk, L) : lo;
+          *reinterpret_cast<u32x4*>(dst + l_off_v1) = tail ? zero_tail(hi, key_blk + 8, L) : hi;
         }
       }
     }
@@ -369,66 +459,210 @@ void sv_attn_partial_lds(AttnArgs a) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
-  if (ntiles > 0) {
-    fetch(0);
-    commit(0, 0);
-  }
+  fetch(0);
+  commit(0, 0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) fetch(t + 1);
     if (active) {
-      const uint8_t* sk = smem + (t & 1) * T::kStage;
-      const uint8_t* sv = sk + 4 * T::kBlk;
       const int kt = r.k_begin + kAttnTile * t;
       const int lb0 = kt / 16;
-      f32x16 x[2];
-      bool live[2];
-      float cs[2][2];
+      float cs[2][2], vs[4];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        live[sb] = kt + 32 * sb < r.k_end;
-        x[sb] = f32x16{};
+      for (int j = 0; j < 4; ++j) {
         if constexpr (FP8) {
-          cs[sb][0] = a.c * a.k_scale[phys_block(a, tbl, lb0 + 2 * sb, n_blk) * a.H_kv + kvh];
-          cs[sb][1] = a.c * a.k_scale[phys_block(a, tbl, lb0 + 2 * sb + 1, n_blk) * a.H_kv + kvh];
+          const size_t pb = phys_block(a, tbl, lb0 + j, n_blk) * a.H_kv + kvh;
+          cs[j >> 1][j & 1] = a.c * a.k_scale[pb];
+          vs[j] = a.v_scale[pb];
         } else {
-          cs[sb][0] = cs[sb][1] = a.c;
-        }
-        if (!live[sb]) continue;
-        const uint8_t* kb = sk + (2 * sb + (r.ql >> 4)) * T::kBlk + (r.ql & 15) * 16;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + (2 * ks + r.hh) * 256);
-          x[sb] = mfma32x32x16(kop, qop[ks], x[sb]);
+          cs[j >> 1][j & 1] = a.c;
+          vs[j] = 1.f;
         }
       }
-      softmax_tile<DB>(x, cs, live, kt, r, m_run, l_run, o);
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (!live[sb]) continue;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          if (kt + 32 * sb + 16 * kk >= r.k_end) continue;
-          float vs = 1.f;
-          if constexpr (FP8) vs = a.v_scale[phys_block(a, tbl, lb0 + 2 * sb + kk, n_blk) * a.H_kv + kvh];
-          const bf16x8 pop = p_operand(x[sb], kk, vs);
-          const uint8_t* vb = sv + (2 * sb + kk) * T::kBlk;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = 32 * db + r.ql;
-            const bf16x8 vop =
-                *reinterpret_cast<const bf16x8*>(vb + (2 * d + (r.hh ^ vhalf_swz(d))) * 16);
-            o[db] = mfma32x32x16(vop, pop, o[db]);
-          }
-        }
-      }
+      const uint8_t* stage = smem + (t & 1) * T::kStage;
+      // every key of the tile exists and every row may see it
+      if (kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P)
+        lds_tile<HD, FP8, false>(a, r, stage, k_lds, v_lds, qop, cs, vs, kt, m_ref, l_run, o);
+      else
+        lds_tile<HD, FP8, true>(a, r, stage, k_lds, v_lds, qop, cs, vs, kt, m_ref, l_run, o);
     }
     if (t + 1 < ntiles) commit(t + 1, (t + 1) & 1);
     __syncthreads();
   }
-  if (active) write_result<HD>(a, r, o, m_run, l_run);
+  if (active) write_result<HD>(a, r, o, m_ref, l_run);
+}
+
+// ---------------------------------------------------------------------------
+// Ring partial kernel (bf16 cache, M > 64): the same tile arithmetic on an
+// NS-stage LDS ring filled by direct global->LDS loads (global_load_lds_dwordx4:
+// lane i of a load writes 16 bytes at the wave's LDS base + 16 i), so NS - 1
+// tiles are in flight while one is computed and no registers hold staging data.
+// Each wave moves K block w and V block w of every tile; the gather addresses
+// carry the slot / half swizzles of the LDS image.  One barrier per tile: the
+// tile's loads are waited for with s_waitcnt vmcnt, then the barrier publishes
+// them and frees the stage computed in the previous iteration for refilling.
+// ---------------------------------------------------------------------------
+template <int HD>
+struct Ring {
+  static constexpr int kLoadsPerBlock = LdsTile<HD>::kBlk / 1024;  // 1 KB per wave load
+  static constexpr int kLoadsPerTile = 2 * kLoadsPerBlock;         // per thread: K and V
+};
+
+#define SV_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with vmcnt = n and the other counters left open.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int HD, bool MASKED>
+__device__ __forceinline__ void ring_tile(const RowCtx& r, const uint8_t* stage, int k_lds,
+                                          int v_lds, const bf16x8 (&qop)[HD / 16], float c,
+                                          int kt, float& m_ref, float& l_run,
+                                          f32x16 (&o)[HD / 32]) {
+  constexpr int KS = HD / 16;
+  constexpr int DB = HD / 32;
+  constexpr int BLK = LdsTile<HD>::kBlk;
+  f32x16 x[2];
+  bool live[2];
+  const float cs[2][2] = {{c, c}, {c, c}};
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    live[sb] = MASKED ? (kt + 32 * sb < r.k_end) : true;
+    x[sb] = f32x16{};
+    if (!live[sb]) continue;
+    const uint8_t* kb = stage + k_lds + 2 * sb * BLK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + ks * 512);
+      x[sb] = mfma32x32x16(kop, qop[ks], x[sb]);
+    }
+  }
+  float alpha;
+  const bool rescale = softmax_core<MASKED>(x, cs, live, kt, r, m_ref, l_run, alpha);
+  auto pv = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if (!live[sb]) continue;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int tk = kt + 32 * sb + 16 * kk;
+        if (MASKED && tk >= r.k_end) continue;
+        const bf16x8 pop = p_operand(x[sb], kk, 1.f);
+        const uint8_t* vb = stage + v_lds + (4 + 2 * sb + kk) * BLK;
+        // the cache block holding slots at or past L has them zeroed here
+        const bool tail = MASKED && tk + 16 > r.L;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
+          if (tail) {
+            const int key0 = tk + 8 * r.hh;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (key0 + j >= r.L) vop[j] = (__bf16)0.f;
+          }
+          o[db] = mfma32x32x16(vop, pop, o[db]);
+        }
+      }
+    }
+  };
+  if (rescale) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+  pv();
+}
+
+// NS stages of LDS per workgroup; WPE workgroups (waves per SIMD) per CU.
+template <int HD, int NS, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void sv_attn_partial_ring(AttnArgs a) {
+  constexpr int KS = HD / 16;
+  constexpr int DB = HD / 32;
+  constexpr int BLK = LdsTile<HD>::kBlk;
+  constexpr int STAGE = LdsTile<HD>::kStage;
+  constexpr int LPB = Ring<HD>::kLoadsPerBlock;
+  constexpr int LPT = Ring<HD>::kLoadsPerTile;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const Work wk = decode_work(a, a.m_tiles);
+  if (!wk.valid) return;
+  const int split = wk.split, kvh = wk.kvh, mt = wk.mt, b = wk.b;
+  const int L = clamp_len(a, b);
+  if (split * a.split_tokens >= L) return;           // whole workgroup: no barrier yet
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int m0 = (mt * 4 + wave) * kRowsPerWave;
+  const bool active = m0 < a.M;                       // inactive waves still load
+  const RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+
+  bf16x8 qop[KS];
+  if (active) load_q<HD, false>(a, r, qop);
+
+  const int32_t* tbl = a.block_table + (size_t)b * a.max_blocks;
+  const int n_blk = (L + 15) / 16;
+  const int ntiles = (r.k_end - r.k_begin + kAttnTile - 1) / kAttnTile;
+  const size_t blk_stride = (size_t)a.H_kv * HD * 32;
+  const uint8_t* kbase = a.k + (size_t)kvh * HD * 32;
+  const uint8_t* vbase = a.v + (size_t)kvh * HD * 32;
+
+  // Gather offsets of this lane for the j-th 1 KB load of a block image.
+  int g_k[LPB], g_v[LPB];
+#pragma unroll
+  for (int j = 0; j < LPB; ++j) {
+    const int p = j * kWave + lane;                    // 16-byte position in the LDS image
+    g_k[j] = ((p >> 4) * 16 + swap23(p & 15)) * 16;
+    g_v[j] = ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16;
+  }
+  auto issue = [&](int t) {
+    const int stage = t % NS;
+    const size_t pb = phys_block(a, tbl, r.k_begin / 16 + 4 * t + wave, n_blk) * blk_stride;
+    const uint8_t* gk = kbase + pb;
+    const uint8_t* gv = vbase + pb;
+    SV_LDS uint8_t* lk = (SV_LDS uint8_t*)(smem + stage * STAGE + wave * BLK);
+    SV_LDS uint8_t* lv = lk + 4 * BLK;
+#pragma unroll
+    for (int j = 0; j < LPB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(gk + g_k[j]), (SV_LDS void*)(lk + j * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < LPB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(gv + g_v[j]), (SV_LDS void*)(lv + j * 1024), 16, 0, 0);
+  };
+
+  const int k_lds = (r.ql >> 4) * BLK + (r.ql & 15) * 16 + r.hh * 256;
+  const int v_lds = (2 * r.ql + (r.hh ^ vhalf_swz(r.ql))) * 16;
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+
+  // Prologue: tiles 0 .. NS-2 in flight (tiles past the end load clamped,
+  // valid blocks and are never computed, keeping the wait counts uniform).
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<(NS - 2) * LPT>();                     // this wave's loads of tile t landed
+    __builtin_amdgcn_s_barrier();                     // ... and every other wave's
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    issue(t + NS - 1);                                // refills the stage freed by tile t-1
+    if (active) {
+      const int kt = r.k_begin + kAttnTile * t;
+      const uint8_t* stage = smem + (t % NS) * STAGE;
+      if (kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P)
+        ring_tile<HD, false>(r, stage, k_lds, v_lds, qop, a.c, kt, m_ref, l_run, o);
+      else
+        ring_tile<HD, true>(r, stage, k_lds, v_lds, qop, a.c, kt, m_ref, l_run, o);
+    }
+  }
+  wait_vmcnt<0>();                                    // drain loads issued past the end
+  if (active) write_result<HD>(a, r, o, m_ref, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -440,10 +674,9 @@ __global__ __launch_bounds__(kWave * NW) void sv_attn_partial_direct(AttnArgs a)
   constexpr int DB = HD / 32;
   constexpr size_t kBlockBytes = (size_t)HD * 16 * (FP8 ? 1 : 2);
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y % a.H_kv;
-  const int mt = blockIdx.y / a.H_kv;
-  const int b = blockIdx.z;
+  const Work wk = decode_work(a, a.m_tiles);
+  if (!wk.valid) return;
+  const int split = wk.split, kvh = wk.kvh, mt = wk.mt, b = wk.b;
   const int L = clamp_len(a, b);
   if (split * a.split_tokens >= L) return;
   const int wave = threadIdx.x / kWave;
@@ -498,7 +731,10 @@ __global__ __launch_bounds__(kWave * NW) void sv_attn_partial_direct(AttnArgs a)
         }
       }
     }
-    softmax_tile<DB>(x, cs, live, kt, r, m_run, l_run, o);
+    if (kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P)
+      softmax_tile<DB, false>(x, cs, live, kt, r, m_run, l_run, o);
+    else
+      softmax_tile<DB, true>(x, cs, live, kt, r, m_run, l_run, o);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       if (!live[sb]) continue;
@@ -612,13 +848,31 @@ void plan_attention(AttnPlan& p, int split_request) {
   p.ws_bytes = p.ws_ml_offset + rows * sizeof(f32x2);
 }
 
+// Partial kernel for row tiles of 128: the LDS ring for bf16 caches, the
+// register-staged double buffer (which decodes e4m3 once per tile) for e4m3.
+template <int HD, bool FP8>
+struct launch_wide;
+template <int HD>
+struct launch_wide<HD, false> {
+  static void run(dim3 grid, const AttnArgs& a, hipStream_t stream) {
+    sv_attn_partial_ring<HD, SV_RING_STAGES, SV_RING_WPE><<<grid, kLdsThreads, 0, stream>>>(a);
+  }
+};
+template <int HD>
+struct launch_wide<HD, true> {
+  static void run(dim3 grid, const AttnArgs& a, hipStream_t stream) {
+    sv_attn_partial_lds<HD, true><<<grid, kLdsThreads, 0, stream>>>(a);
+  }
+};
+
 template <int HD, bool FP8>
 static hipError_t launch_typed(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
-  dim3 grid(p.s_max, p.H_kv * p.m_tiles, p.B);
+  const long long units = (long long)p.s_max * p.B * p.H_kv;
+  dim3 grid((unsigned)(((units + 7) / 8) * 8 * p.m_tiles));
   switch (p.waves) {
     case 1: sv_attn_partial_direct<HD, FP8, 1><<<grid, kWave * 1, 0, stream>>>(a); break;
     case 2: sv_attn_partial_direct<HD, FP8, 2><<<grid, kWave * 2, 0, stream>>>(a); break;
-    default: sv_attn_partial_lds<HD, FP8><<<grid, kLdsThreads, 0, stream>>>(a); break;
+    default: launch_wide<HD, FP8>::run(grid, a, stream); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.s_max <= 1) return e;
@@ -640,6 +894,7 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   a.ws_o = static_cast<float*>(ptr.ws);
   a.ws_ml = p.ws_bytes ? reinterpret_cast<f32x2*>(static_cast<char*>(ptr.ws) + p.ws_ml_offset)
                        : nullptr;
+  a.B = p.B;
   a.R = p.R;
   a.H_q = p.H_q;
   a.H_kv = p.H_kv;
@@ -650,6 +905,7 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   a.max_kv_len = p.max_kv_len;
   a.split_tokens = p.split_tokens;
   a.s_max = p.s_max;
+  a.m_tiles = p.m_tiles;
   a.c = p.sm_scale * kLog2e;
   if (p.hd == 128)
     return p.fp8 ? launch_typed<128, true>(p, a, stream) : launch_typed<128, false>(p, a, stream);

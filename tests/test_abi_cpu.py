@@ -204,3 +204,11 @@ def test_binding_raises_sv_error():
         sv.spec_accept_workspace_size(0, 1, 1)
     assert e.value.status == sv.SV_ERR_INVALID
     assert "batch" in str(e.value)
+
+
+def test_every_kernel_launch_stub_is_defined():
+    """A kernel whose host-side launch stub was dropped at compile time shows up
+    as an undefined __device_stub__ symbol: loading would fail on first use."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", sv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "__device_stub__" not in out
