@@ -59,7 +59,9 @@ struct AttnArgs {
   int B, R, H_q, H_kv, G, M;
   int max_blocks, num_blocks, max_kv_len;
   int split_tokens, s_max, m_tiles;
+  int min_tiles;  // stream-K: least tiles per workgroup
   float c;        // sm_scale * log2(e)
+  int* sk_meta;   // stream-K: [W, Wp, pref[0..B]] written by workgroup 0 for the merge
 };
 
 // Row i of the 32-key score block holds key pi(i) of that block.
@@ -288,6 +290,10 @@ constexpr int kLdsThreads = 256;
 #define SV_RING_STAGES 2
 #define SV_RING_WPE 2
 #endif
+#ifndef SV_STREAM_STAGES
+#define SV_STREAM_STAGES 2
+#define SV_STREAM_WPE 2
+#endif
 
 template <int HD>
 struct LdsTile {
@@ -325,6 +331,9 @@ struct Stager {
 
 // One 64-key tile: S^T = K . Q^T on the LDS image, online-softmax update, and
 // O^T += V^T . P^T.
+// One 64-key tile on the LDS image of the register-staged kernel.  V slots at
+// or past L were zeroed when the tile was staged; masked tiles still run every
+// MFMA (see ring_tile) and exclude keys by selects on the scores.
 template <int HD, bool FP8, bool MASKED>
 __device__ __forceinline__ void lds_tile(const AttnArgs& a, const RowCtx& r, const uint8_t* stage,
                                          int k_lds, int v_lds, const bf16x8 (&qop)[HD / 16],
@@ -339,7 +348,6 @@ __device__ __forceinline__ void lds_tile(const AttnArgs& a, const RowCtx& r, con
   for (int sb = 0; sb < 2; ++sb) {
     live[sb] = MASKED ? (kt + 32 * sb < r.k_end) : true;
     x[sb] = f32x16{};
-    if (!live[sb]) continue;
     const uint8_t* kb = stage + k_lds + 2 * sb * BLK;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -350,10 +358,8 @@ __device__ __forceinline__ void lds_tile(const AttnArgs& a, const RowCtx& r, con
   softmax_tile<DB, MASKED>(x, cs, live, kt, r, m_ref, l_run, o);
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    if (!live[sb]) continue;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      if (MASKED && kt + 32 * sb + 16 * kk >= r.k_end) continue;
       const bf16x8 pop = p_operand(x[sb], kk, FP8 ? vs[2 * sb + kk] : 1.f);
       const uint8_t* vb = stage + v_lds + (4 + 2 * sb + kk) * BLK;
 #pragma unroll
@@ -519,6 +525,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// One 64-key tile of the bf16 LDS image.  Masked tiles (the causal tail or the
+// end of the sequence) run every MFMA like unmasked ones: keys past the end are
+// excluded by selects on the scores and their V values are zeroed by selects,
+// never by skipping work -- MFMA instructions do not observe the EXEC mask, so a
+// branch the compiler turns into lane masking would still multiply poison V
+// by zero probabilities (NaN).
 template <int HD, bool MASKED>
 __device__ __forceinline__ void ring_tile(const RowCtx& r, const uint8_t* stage, int k_lds,
                                           int v_lds, const bf16x8 (&qop)[HD / 16], float c,
@@ -534,7 +546,6 @@ __device__ __forceinline__ void ring_tile(const RowCtx& r, const uint8_t* stage,
   for (int sb = 0; sb < 2; ++sb) {
     live[sb] = MASKED ? (kt + 32 * sb < r.k_end) : true;
     x[sb] = f32x16{};
-    if (!live[sb]) continue;
     const uint8_t* kb = stage + k_lds + 2 * sb * BLK;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -544,37 +555,28 @@ __device__ __forceinline__ void ring_tile(const RowCtx& r, const uint8_t* stage,
   }
   float alpha;
   const bool rescale = softmax_core<MASKED>(x, cs, live, kt, r, m_ref, l_run, alpha);
-  auto pv = [&]() {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if (!live[sb]) continue;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int tk = kt + 32 * sb + 16 * kk;
-        if (MASKED && tk >= r.k_end) continue;
-        const bf16x8 pop = p_operand(x[sb], kk, 1.f);
-        const uint8_t* vb = stage + v_lds + (4 + 2 * sb + kk) * BLK;
-        // the cache block holding slots at or past L has them zeroed here
-        const bool tail = MASKED && tk + 16 > r.L;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
-          if (tail) {
-            const int key0 = tk + 8 * r.hh;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (key0 + j >= r.L) vop[j] = (__bf16)0.f;
-          }
-          o[db] = mfma32x32x16(vop, pop, o[db]);
-        }
-      }
-    }
-  };
   if (rescale) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
   }
-  pv();
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int key0 = kt + 32 * sb + 16 * kk + 8 * r.hh;   // first key of this lane's 8
+      const bf16x8 pop = p_operand(x[sb], kk, 1.f);
+      const uint8_t* vb = stage + v_lds + (4 + 2 * sb + kk) * BLK;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
+        if constexpr (MASKED) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vop[j] = key0 + j < r.L ? vop[j] : (__bf16)0.f;
+        }
+        o[db] = mfma32x32x16(vop, pop, o[db]);
+      }
+    }
+  }
 }
 
 // NS stages of LDS per workgroup; WPE workgroups (waves per SIMD) per CU.
@@ -666,6 +668,288 @@ void sv_attn_partial_ring(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Stream-K persistent kernel (bf16 cache, row tiles of 128).
+//
+// Work is the list of (sequence b, KV head, row tile, 64-key tile) in that
+// order: unit u = (b, kvh, mt) owns T_b = ceil(L_b / 64) consecutive tiles.
+// A fixed grid of P workgroups splits the W tiles of the whole batch into equal
+// contiguous ranges of Wp = max(ceil(W / P), min_tiles) tiles, so every
+// workgroup streams the same number of tiles regardless of how ragged the
+// lengths are, and its LDS ring stays full across unit boundaries.  A unit
+// whose tiles all fall in one range is finished in place (O / l written as
+// bf16); a unit cut by range boundaries leaves one unnormalised (O, m, l)
+// segment per range -- at most the first and the last segment of each range
+// -- which sv_attn_streamk_merge combines with the split-merge rule.
+// Every workgroup computes the per-sequence tile prefix from kv_lens in LDS;
+// workgroup 0 also stores it (with W and Wp) for the merge kernel.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxBatch = 2048;
+constexpr int kStreamRows = 128;          // rows per unit (4 waves x 32)
+
+// pref[b] = tiles of all units of sequences before b, for b = 0 .. B.
+__device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* wsum) {
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int per_seq = a.H_kv * a.m_tiles;
+  const int chunk = (a.B + kLdsThreads - 1) / kLdsThreads;
+  const int lo = min(tid * chunk, a.B), hi = min(lo + chunk, a.B);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) {
+    sum += ((clamp_len(a, b) + kAttnTile - 1) / kAttnTile) * per_seq;
+    pref[b + 1] = sum;                      // inclusive within this thread's chunk
+  }
+  // exclusive scan of the per-thread sums: within each wave, then across waves
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const int excl = base + incl - sum;
+  for (int b = lo; b < hi; ++b) pref[b + 1] += excl;
+  if (tid == 0) pref[0] = 0;
+  __syncthreads();
+}
+
+// Position in the work list: sequence b, unit ul = kvh * m_tiles + mt within
+// the sequence, tile within the unit, and the unit's tile count T.
+struct Cursor {
+  int b, ul, tile, T;
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, const int* pref, int g) {
+  int lo = 0, hi = a.B;                     // pref[lo] <= g < pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uniform(pref[mid]) <= g) lo = mid; else hi = mid;
+  }
+  const int per_seq = a.H_kv * a.m_tiles;
+  Cursor c;
+  c.b = lo;
+  c.T = uniform((pref[lo + 1] - pref[lo]) / per_seq);
+  const int r = g - uniform(pref[lo]);
+  c.ul = r / c.T;
+  c.tile = r % c.T;
+  return c;
+}
+
+__device__ __forceinline__ void cursor_next(const AttnArgs& a, const int* pref, Cursor& c) {
+  if (++c.tile < c.T) return;
+  c.tile = 0;
+  if (++c.ul < a.H_kv * a.m_tiles) return;
+  c.ul = 0;
+  do {
+    ++c.b;
+  } while (c.b < a.B && uniform(pref[c.b + 1]) == uniform(pref[c.b]));
+  if (c.b < a.B) c.T = uniform((pref[c.b + 1] - pref[c.b]) / (a.H_kv * a.m_tiles));
+}
+
+template <int HD, int NS, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void sv_attn_streamk(AttnArgs a) {
+  constexpr int KS = HD / 16;
+  constexpr int DB = HD / 32;
+  constexpr int BLK = LdsTile<HD>::kBlk;
+  constexpr int STAGE = LdsTile<HD>::kStage;
+  constexpr int LPB = Ring<HD>::kLoadsPerBlock;
+  constexpr int LPT = Ring<HD>::kLoadsPerTile;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  __shared__ int s_pref[kStreamMaxBatch + 1];
+  __shared__ int s_wsum[kLdsThreads / kWave];
+
+  build_prefix(a, s_pref, s_wsum);
+  const int W = uniform(s_pref[a.B]);
+  const int Wp = max((W + (int)gridDim.x - 1) / (int)gridDim.x, a.min_tiles);
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    for (int b = tid; b <= a.B; b += kLdsThreads) a.sk_meta[2 + b] = s_pref[b];
+    if (tid == 0) {
+      a.sk_meta[0] = W;
+      a.sk_meta[1] = Wp;
+    }
+  }
+  const int g0 = (int)blockIdx.x * Wp;
+  const int g1 = min(g0 + Wp, W);
+  if (g0 >= g1) return;                       // whole workgroup, after the last barrier use
+
+  const int wave = uniform(tid / kWave);
+  const int lane = tid % kWave;
+  const int ql = lane & 31, hh = lane >> 5;
+  const size_t blk_stride = (size_t)a.H_kv * HD * 32;
+
+  // gather offsets of this lane for the j-th 1 KB load of a block image
+  int g_k[LPB], g_v[LPB];
+#pragma unroll
+  for (int j = 0; j < LPB; ++j) {
+    const int p = j * kWave + lane;
+    g_k[j] = ((p >> 4) * 16 + swap23(p & 15)) * 16;
+    g_v[j] = ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16;
+  }
+  const int k_lds = (ql >> 4) * BLK + (ql & 15) * 16 + hh * 256;
+  const int v_lds = (2 * ql + (hh ^ vhalf_swz(ql))) * 16;
+
+  // Loads of one tile: wave w moves K and V of the tile's cache block w.
+  auto issue = [&](const Cursor& c, int stage) {
+    const int L = clamp_len(a, c.b);
+    const int n_blk = (L + 15) / 16;
+    const int32_t* tbl = a.block_table + (size_t)c.b * a.max_blocks;
+    const int kvh = c.ul / a.m_tiles;
+    const size_t pb = phys_block(a, tbl, 4 * c.tile + wave, n_blk) * blk_stride + (size_t)kvh * HD * 32;
+    const uint8_t* gk = a.k + pb;
+    const uint8_t* gv = a.v + pb;
+    SV_LDS uint8_t* lk = (SV_LDS uint8_t*)(smem + stage * STAGE + wave * BLK);
+    SV_LDS uint8_t* lv = lk + 4 * BLK;
+#pragma unroll
+    for (int j = 0; j < LPB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(gk + g_k[j]), (SV_LDS void*)(lk + j * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < LPB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(gv + g_v[j]), (SV_LDS void*)(lv + j * 1024), 16, 0, 0);
+  };
+
+  Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load
+  Cursor cc = ci;                             // tile being computed
+  int gi = g0;
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {
+    issue(ci, k);
+    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    ++gi;
+  }
+
+  RowCtx r;
+  bool active = false;
+  int seg_start = g0;
+  bf16x8 qop[KS];
+  f32x16 o[DB];
+  float m_ref = -INFINITY, l_run = 0.f;
+
+  for (int g = g0; g < g1; ++g) {
+    const int t = g - g0;
+    wait_vmcnt<(NS - 2) * LPT>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    issue(ci, (t + NS - 1) % NS);             // refills the stage freed by tile g - 1
+    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    ++gi;
+
+    if (cc.tile == 0 || g == g0) {             // a new segment starts
+      seg_start = g;
+      const int kvh = cc.ul / a.m_tiles;
+      const int mt = cc.ul % a.m_tiles;
+      const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+      active = m0 < a.M;
+      const int L = clamp_len(a, cc.b);
+      r = make_row_ctx(a, 0, kvh, cc.b, L, m0, lane);
+      r.k_end = L;
+      if (active) load_q<HD, false>(a, r, qop);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+      m_ref = -INFINITY;
+      l_run = 0.f;
+    }
+    if (active) {
+      const int kt = cc.tile * kAttnTile;
+      const uint8_t* stage = smem + (t % NS) * STAGE;
+      if (kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P)
+        ring_tile<HD, false>(r, stage, k_lds, v_lds, qop, a.c, kt, m_ref, l_run, o);
+      else
+        ring_tile<HD, true>(r, stage, k_lds, v_lds, qop, a.c, kt, m_ref, l_run, o);
+    }
+    if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
+      if (active) {
+        const bool whole = cc.tile == cc.T - 1 && seg_start == g - cc.tile;
+        if (whole) {
+          r.n_splits = 1;
+          write_result<HD>(a, r, o, m_ref, l_run);
+        } else {
+          // slot 0: the range's first segment; slot 1: its last one
+          const int slot = seg_start == g0 ? 0 : 1;
+          const float l_tot = halves_sum(l_run);
+          if (r.row_ok) {
+            const size_t srow = ((size_t)blockIdx.x * 2 + slot) * kStreamRows + wave * kRowsPerWave + ql;
+            float* dst = a.ws_o + srow * HD;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 32 * db + 8 * q4 + 4 * hh;
+                *reinterpret_cast<f32x4*>(dst + d) =
+                    f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
+              }
+            if (hh == 0) a.ws_ml[srow] = f32x2{m_ref, l_tot};
+          }
+        }
+      }
+    }
+    if (g + 1 < g1) cursor_next(a, s_pref, cc);
+  }
+  wait_vmcnt<0>();                            // drain loads issued past the range
+}
+
+// Combines the segments of units that straddle range boundaries.  One wave per
+// (unit, row); a unit's tiles [C, C + T) were split over ranges
+// i = C / Wp .. (C + T - 1) / Wp, and range i holds its segment in slot 0 when
+// the range starts inside the unit, else (the unit began earlier) in slot 1.
+template <int HD>
+__global__ __launch_bounds__(256) void sv_attn_streamk_merge(AttnArgs a) {
+  constexpr int PER = HD / kWave;
+  constexpr int WG_PER_UNIT = kStreamRows / 4;
+  const int unit = blockIdx.x / WG_PER_UNIT;
+  const int r128 = (blockIdx.x % WG_PER_UNIT) * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int per_seq = a.H_kv * a.m_tiles;
+  const int b = unit / per_seq;
+  const int ul = unit % per_seq;
+  const int kvh = ul / a.m_tiles;
+  const int mt = ul % a.m_tiles;
+  const int m = mt * kStreamRows + r128;
+  if (b >= a.B || m >= a.M) return;
+  const int Wp = a.sk_meta[1];
+  const int* pref = a.sk_meta + 2;
+  const int T = (pref[b + 1] - pref[b]) / per_seq;
+  if (T == 0) return;
+  const int C = pref[b] + ul * T;
+  const int i0 = C / Wp, i1 = (C + T - 1) / Wp;
+  if (i0 == i1) return;                       // finished in place
+  float mx = -INFINITY;
+  for (int i = i0; i <= i1; ++i) {
+    const int slot = i * Wp >= C ? 0 : 1;
+    mx = fmaxf(mx, a.ws_ml[((size_t)i * 2 + slot) * kStreamRows + r128][0]);
+  }
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float acc[PER] = {};
+  float l = 0.f;
+  for (int i = i0; i <= i1; ++i) {
+    const int slot = i * Wp >= C ? 0 : 1;
+    const size_t rr = ((size_t)i * 2 + slot) * kStreamRows + r128;
+    const f32x2 ml = a.ws_ml[rr];
+    const float w = fast_exp2(ml[0] - mu);
+    l += w * ml[1];
+    const float* src = a.ws_o + rr * HD + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w * src[e];
+  }
+  const float inv = 1.f / l;
+  const int pos = m / a.G;
+  const int head = kvh * a.G + m % a.G;
+  uint16_t* orow = a.out + ((size_t)(b * a.R + pos) * a.H_q + head) * HD + lane * PER;
+  if constexpr (PER == 2) {
+    *reinterpret_cast<uint32_t*>(orow) =
+        (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+  } else {
+    orow[0] = f32_to_bf16_bits(acc[0] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Direct partial kernel (M <= 64): every wave streams its own operands.
 // ---------------------------------------------------------------------------
 template <int HD, bool FP8, int NW>
@@ -713,7 +997,7 @@ __global__ __launch_bounds__(kWave * NW) void sv_attn_partial_direct(AttnArgs a)
         cs[sb][1] *= a.k_scale[blk[sb][1] * a.H_kv + kvh];
       }
       x[sb] = f32x16{};
-      if (!live[sb]) continue;
+      // dead sub-blocks still run (on a clamped, valid block): see ring_tile
       const uint8_t* kb = a.k + (blk[sb][krow >> 4] * a.H_kv + kvh) * kBlockBytes;
       const int slot = krow & 15;
       if constexpr (!FP8) {
@@ -731,23 +1015,21 @@ __global__ __launch_bounds__(kWave * NW) void sv_attn_partial_direct(AttnArgs a)
         }
       }
     }
-    if (kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P)
+    const bool masked = !(kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P);
+    if (!masked)
       softmax_tile<DB, false>(x, cs, live, kt, r, m_run, l_run, o);
     else
       softmax_tile<DB, true>(x, cs, live, kt, r, m_run, l_run, o);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      if (!live[sb]) continue;
       const int t0 = kt + 32 * sb;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int tk = t0 + 16 * kk;   // first key of this cache block
-        if (tk >= r.k_end) continue;
         float vs = 1.f;
         if constexpr (FP8) vs = a.v_scale[blk[sb][kk] * a.H_kv + kvh];
         const bf16x8 pop = p_operand(x[sb], kk, vs);
         const uint8_t* vb = a.v + (blk[sb][kk] * a.H_kv + kvh) * kBlockBytes;
-        const bool tail = tk + 16 > L;   // block holds slots past L: zero them
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int d = 32 * db + r.ql;
@@ -758,10 +1040,9 @@ __global__ __launch_bounds__(kWave * NW) void sv_attn_partial_direct(AttnArgs a)
             const u32x2 raw = *reinterpret_cast<const u32x2*>(vb + d * 16 + 8 * r.hh);
             vop = e4m3x8_to_bf16(raw[0], raw[1]);
           }
-          if (tail) {
+          if (masked) {   // slots at or past L (poison, or a clamped block) become 0
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (tk + 8 * r.hh + j >= L) vop[j] = (__bf16)0.f;
+            for (int j = 0; j < 8; ++j) vop[j] = tk + 8 * r.hh + j < L ? vop[j] : (__bf16)0.f;
           }
           o[db] = mfma32x32x16(vop, pop, o[db]);
         }
@@ -819,12 +1100,33 @@ __global__ __launch_bounds__(256) void sv_attn_combine(AttnArgs a, int total_row
   }
 }
 
+// Stream-K variant: LDS stages per workgroup and workgroups per CU.
+constexpr int kStreamStages = SV_STREAM_STAGES;
+constexpr int kStreamWPE = SV_STREAM_WPE;
+constexpr int kStreamCUs = 256;            // MI355X compute units
+constexpr int kStreamDefaultMinTiles = 8;
+
 void plan_attention(AttnPlan& p, int split_request) {
   p.G = p.H_q / p.H_kv;
   p.M = p.G * p.R;
   const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
   p.waves = waves_needed > 2 ? 4 : waves_needed;
   p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);
+  p.streamk = !p.fp8 && p.waves == 4 && p.B <= kStreamMaxBatch;
+  if (p.streamk) {
+    // one split per unit as far as the row context goes; ranges come from min_tiles
+    p.split_tokens = (p.max_kv_len + kAttnTile - 1) / kAttnTile * kAttnTile;
+    p.s_max = 1;
+    p.sk_wgs = kStreamCUs * kStreamWPE;
+    p.min_tiles = split_request > 0 ? split_request / kAttnTile : kStreamDefaultMinTiles;
+    const size_t slots = (size_t)p.sk_wgs * 2 * kStreamRows;
+    p.ws_meta_offset = 0;
+    const size_t meta_bytes = ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256;
+    p.ws_o_bytes = slots * p.hd * sizeof(float);
+    p.ws_ml_offset = meta_bytes + p.ws_o_bytes;
+    p.ws_bytes = p.ws_ml_offset + slots * sizeof(f32x2);
+    return;
+  }
   int split = split_request;
   if (split <= 0) {
     // Aim at roughly 2048 workgroups for the longest sequences (8 per compute
@@ -838,6 +1140,7 @@ void plan_attention(AttnPlan& p, int split_request) {
   }
   p.split_tokens = split;
   p.s_max = (p.max_kv_len + split - 1) / split;
+  p.ws_meta_offset = 0;
   if (p.s_max <= 1) {
     p.ws_o_bytes = p.ws_ml_offset = p.ws_bytes = 0;
     return;
@@ -846,6 +1149,16 @@ void plan_attention(AttnPlan& p, int split_request) {
   p.ws_o_bytes = rows * p.hd * sizeof(float);
   p.ws_ml_offset = (p.ws_o_bytes + 255) / 256 * 256;
   p.ws_bytes = p.ws_ml_offset + rows * sizeof(f32x2);
+}
+
+template <int HD>
+static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
+  sv_attn_streamk<HD, kStreamStages, kStreamWPE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int units = p.B * p.H_kv * p.m_tiles;
+  sv_attn_streamk_merge<HD><<<units * (kStreamRows / 4), 256, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 // Partial kernel for row tiles of 128: the LDS ring for bf16 caches, the
@@ -891,9 +1204,16 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   a.block_table = ptr.block_table;
   a.kv_lens = ptr.kv_lens;
   a.out = static_cast<uint16_t*>(ptr.out);
-  a.ws_o = static_cast<float*>(ptr.ws);
-  a.ws_ml = p.ws_bytes ? reinterpret_cast<f32x2*>(static_cast<char*>(ptr.ws) + p.ws_ml_offset)
-                       : nullptr;
+  char* ws = static_cast<char*>(ptr.ws);
+  if (p.streamk) {
+    a.sk_meta = reinterpret_cast<int*>(ws + p.ws_meta_offset);
+    a.ws_o = reinterpret_cast<float*>(ws + ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256);
+  } else {
+    a.sk_meta = nullptr;
+    a.ws_o = reinterpret_cast<float*>(ws);
+  }
+  a.ws_ml = p.ws_bytes ? reinterpret_cast<f32x2*>(ws + p.ws_ml_offset) : nullptr;
+  a.min_tiles = p.min_tiles;
   a.B = p.B;
   a.R = p.R;
   a.H_q = p.H_q;
@@ -907,6 +1227,7 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   a.s_max = p.s_max;
   a.m_tiles = p.m_tiles;
   a.c = p.sm_scale * kLog2e;
+  if (p.streamk) return p.hd == 128 ? launch_streamk<128>(p, a, stream) : launch_streamk<64>(p, a, stream);
   if (p.hd == 128)
     return p.fp8 ? launch_typed<128, true>(p, a, stream) : launch_typed<128, false>(p, a, stream);
   return p.fp8 ? launch_typed<64, true>(p, a, stream) : launch_typed<64, false>(p, a, stream);

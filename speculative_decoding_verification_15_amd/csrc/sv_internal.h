@@ -23,6 +23,11 @@ struct AttnPlan {
   int s_max;         // ceil(max_kv_len / split_tokens)
   int waves;         // waves per workgroup (each owns 32 query rows)
   int m_tiles;       // ceil(M / (32 * waves))
+  // stream-K path (bf16 cache, 128-row tiles): persistent workgroups, the least
+  // number of 64-key tiles per workgroup, and the metadata block in the workspace
+  bool streamk;
+  int sk_wgs, min_tiles;
+  size_t ws_meta_offset;
   size_t ws_o_bytes, ws_ml_offset, ws_bytes;
 };
 

@@ -147,15 +147,21 @@ def test_attn_fp8_needs_scales_and_workspace_size():
 
 
 def test_attn_workspace_size_formula():
-    # one split: no workspace
-    p = good_params(max_kv_len=1000, split_tokens=1024)
+    # split-K path (e4m3 cache): one split needs no workspace
+    p = good_params(max_kv_len=1000, split_tokens=1024, kv_dtype=sv.SV_KV_FP8_E4M3)
     assert sv.spec_verify_attn_workspace_size(p) == 0
     # four splits of 256 keys: O (hd floats) and (m, l) per split and query row
-    p = good_params(max_kv_len=1000, split_tokens=256)
+    p = good_params(max_kv_len=1000, split_tokens=256, kv_dtype=sv.SV_KV_FP8_E4M3)
     B, H_kv, S, M, hd = 4, 8, 4, 8 * 16, 128
     rows = B * H_kv * S * M
     o_bytes = rows * hd * 4
     assert sv.spec_verify_attn_workspace_size(p) == (o_bytes + 255) // 256 * 256 + rows * 8
+    # stream-K path (bf16, 128 rows per KV head): metadata (W, Wp, B + 1 prefix
+    # entries) then two (O, m, l) slots of 128 rows for each of 512 workgroups
+    p = good_params(max_kv_len=1000)
+    slots = 512 * 2 * 128
+    meta = ((4 + 3) * 4 + 255) // 256 * 256
+    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
 
 
 @pytest.mark.parametrize("B,D,V,status", [

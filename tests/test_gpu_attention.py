@@ -106,3 +106,22 @@ def test_split_results_agree_closely():
     many = DeviceAttn.to_f64(d.run(64))
     # different merge orders round differently, but only at bf16 resolution
     assert np.abs(one - many).max() <= 2 * 2.0 ** -8 * np.abs(one).max()
+
+
+# Lengths whose last 64-key tile holds 1, 5, 16, 31, 32, 33, 63 or 64 keys: the
+# tile's second 32-key sub-block (or most of it) lies past the end of the
+# sequence, where the cache holds poison.
+TAIL_REMAINDERS = [1, 5, 16, 31, 32, 33, 63, 64]
+
+
+@pytest.mark.parametrize("split", [0, 64, 1 << 20])
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15", "mini_gqa4_d7", "mini_mqa_d16"])
+def test_attention_dead_tail_subblocks(name, split):
+    w = MINI[name]
+    L = np.array([64 * (3 + i) + rem for i, rem in enumerate(TAIL_REMAINDERS)])
+    w = w.replace(B=len(L))
+    inp = make_attn_inputs(w, T_override=L - w.R)
+    assert (inp.kv_lens == L).all()
+    gpu = run_attention(inp, split_tokens=split)
+    assert np.isfinite(gpu).all()
+    check(gpu, oracle_for(inp), f"{name}/tails/split={split}")
