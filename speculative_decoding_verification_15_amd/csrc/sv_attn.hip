@@ -216,6 +216,45 @@ __device__ __forceinline__ bool softmax_core(f32x16 (&x)[2], const float (&cs)[2
   return __ballot(move) != 0;
 }
 
+// Online-softmax update for one 32-key sub-block (scores x, scale c into the
+// log2 domain; MASKED: masked scores are already -inf, and a row may have no
+// visible key yet).  Returns the probabilities as the PV B operands of its two
+// 16-key halves, with l accumulated from those bf16 values (the same numbers
+// the PV product multiplies), and whether O must be rescaled by alpha (lazy
+// reference, see softmax_core).
+template <bool MASKED = false>
+__device__ __forceinline__ bool softmax_sub(const f32x16& x, float c, float& m_ref, float& l_run,
+                                            float& alpha, bf16x8& p0, bf16x8& p1) {
+  float hm = x[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) hm = fmaxf(hm, x[v]);
+  const float tmax = halves_max(hm * c);
+  bool move = false;
+  alpha = 1.f;
+  if (m_ref == -INFINITY) {
+    m_ref = tmax;
+  } else if (tmax > m_ref + kLazyRescale) {
+    alpha = fast_exp2(m_ref - tmax);
+    m_ref = tmax;
+    move = true;
+  }
+  const float m_neg = (MASKED && m_ref == -INFINITY) ? 0.f : -m_ref;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p0[j] = (__bf16)fast_exp2(__builtin_fmaf(x[j], c, m_neg));
+    p1[j] = (__bf16)fast_exp2(__builtin_fmaf(x[8 + j], c, m_neg));
+  }
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[j], p0[j + 1]}, one, psum, false);
+    psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[j], p1[j + 1]}, one, psum, false);
+  }
+  l_run = l_run * alpha + psum;
+  return __ballot(move) != 0;
+}
+
 // Online-softmax update plus the O rescale in place (used by the direct kernel).
 template <int DB, bool MASKED>
 __device__ __forceinline__ void softmax_tile(f32x16 (&x)[2], const float (&cs)[2][2],
@@ -290,8 +329,7 @@ constexpr int kLdsThreads = 256;
 #define SV_RING_STAGES 2
 #define SV_RING_WPE 2
 #endif
-#ifndef SV_STREAM_STAGES
-#define SV_STREAM_STAGES 2
+#ifndef SV_STREAM_WPE
 #define SV_STREAM_WPE 2
 #endif
 
@@ -517,12 +555,42 @@ struct Ring {
 };
 
 #define SV_LDS __attribute__((address_space(3)))
+#define SV_CONST __attribute__((address_space(4)))
 
 // s_waitcnt with vmcnt = n and the other counters left open.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS byte address of a shared-memory location (the value M0 takes).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(SV_LDS const void*)p;
+}
+
+// 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4: lane
+// i's bytes land at lds + 16 i; NT: non-temporal, for data read exactly once).
+// Written as inline assembly so that the compiler does not track it: its own
+// bookkeeping makes every later LDS read wait for all such loads in flight (it
+// cannot tell which ring stage a load fills), which would drain the ring each
+// tile.  Callers order these loads with s_waitcnt vmcnt and a barrier
+// themselves; loads unknown to the compiler only make its own vmcnt waits more
+// conservative, never less.  The statement sets M0, so a kernel using it must
+// hold no other value in M0 (no LDS-DMA builtins, no indirect register
+// indexing); the stream-K kernel has no other M0 user.
+template <bool NT>
+__device__ __forceinline__ void dma_to_lds16(const void* src, uint32_t lds) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
 }
 
 // One 64-key tile of the bf16 LDS image.  Masked tiles (the causal tail or the
@@ -552,6 +620,29 @@ __device__ __forceinline__ void ring_tile(const RowCtx& r, const uint8_t* stage,
       const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + ks * 512);
       x[sb] = mfma32x32x16(kop, qop[ks], x[sb]);
     }
+  }
+  if constexpr (!MASKED) {
+    // Sub-block by sub-block: the VALU softmax of one sub-block is independent
+    // of the other sub-block's MFMAs, so the two overlap within the wave.
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      float alpha;
+      bf16x8 p[2];
+      if (softmax_sub(x[sb], c, m_ref, l_run, alpha, p[0], p[1])) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint8_t* vb = stage + v_lds + (4 + 2 * sb + kk) * BLK;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
+          o[db] = mfma32x32x16(vop, p[kk], o[db]);
+        }
+      }
+    }
+    return;
   }
   float alpha;
   const bool rescale = softmax_core<MASKED>(x, cs, live, kt, r, m_ref, l_run, alpha);
@@ -670,8 +761,8 @@ void sv_attn_partial_ring(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Stream-K persistent kernel (bf16 cache, row tiles of 128).
 //
-// Work is the list of (sequence b, KV head, row tile, 64-key tile) in that
-// order: unit u = (b, kvh, mt) owns T_b = ceil(L_b / 64) consecutive tiles.
+// Work is the list of (sequence b, KV head, row tile, 32-key tile) in that
+// order: unit u = (b, kvh, mt) owns T_b = ceil(L_b / 32) consecutive tiles.
 // A fixed grid of P workgroups splits the W tiles of the whole batch into equal
 // contiguous ranges of Wp = max(ceil(W / P), min_tiles) tiles, so every
 // workgroup streams the same number of tiles regardless of how ragged the
@@ -682,9 +773,28 @@ void sv_attn_partial_ring(AttnArgs a) {
 // -- which sv_attn_streamk_merge combines with the split-merge rule.
 // Every workgroup computes the per-sequence tile prefix from kv_lens in LDS;
 // workgroup 0 also stores it (with W and Wp) for the merge kernel.
+//
+// A tile is one 32-key sub-block (16 KB of K and V at hd 128), so the 64 KB
+// ring of each of the two workgroups on a compute unit holds four stages and
+// keeps three tiles of loads in flight while one is computed: at the HBM
+// latency it is the bytes in flight, not the issue rate, that bound the
+// bandwidth a workgroup draws.
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxBatch = 2048;
 constexpr int kStreamRows = 128;          // rows per unit (4 waves x 32)
+constexpr int kSkKeys = 32;               // keys per stream-K tile
+
+#ifndef SV_STREAM_RING_BYTES
+#define SV_STREAM_RING_BYTES 65536
+#endif
+
+template <int HD>
+struct SkTile {
+  static constexpr int kBlk = LdsTile<HD>::kBlk;   // one 16-key block of K or V
+  static constexpr int kStage = 4 * kBlk;          // K blocks 0, 1, then V blocks 0, 1
+  static constexpr int kLoads = kBlk / 1024;       // 1 KB wave loads per block
+  static constexpr int kStages = SV_STREAM_RING_BYTES / kStage;
+};
 
 // pref[b] = tiles of all units of sequences before b, for b = 0 .. B.
 __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* wsum) {
@@ -695,7 +805,7 @@ __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* 
   const int lo = min(tid * chunk, a.B), hi = min(lo + chunk, a.B);
   int sum = 0;
   for (int b = lo; b < hi; ++b) {
-    sum += ((clamp_len(a, b) + kAttnTile - 1) / kAttnTile) * per_seq;
+    sum += ((clamp_len(a, b) + kSkKeys - 1) / kSkKeys) * per_seq;
     pref[b + 1] = sum;                      // inclusive within this thread's chunk
   }
   // exclusive scan of the per-thread sums: within each wave, then across waves
@@ -750,16 +860,77 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, const int* pref, 
   if (c.b < a.B) c.T = uniform((pref[c.b + 1] - pref[c.b]) / (a.H_kv * a.m_tiles));
 }
 
-template <int HD, int NS, int WPE>
+// Zeroes the V values of keys >= L in the tile image at stage (keys kt ..
+// kt + 31), so that poison past the end of the sequence never meets the zero
+// probabilities of those keys in the PV product (MFMA instructions do not
+// observe the EXEC mask, so lane masking could not keep it out).
+template <int HD>
+__device__ __forceinline__ void sk_zero_v_tail(uint8_t* stage, int kt, int L) {
+  constexpr int BLK = SkTile<HD>::kBlk;
+  constexpr int POS = 2 * HD;                // 16-byte vectors per V block image
+  for (int i = threadIdx.x; i < 2 * POS; i += kLdsThreads) {
+    const int bk = i / POS, p = i % POS;
+    const int d = p >> 1, h = (p & 1) ^ vhalf_swz(d);
+    const int key0 = kt + 16 * bk + 8 * h;
+    if (key0 + 8 > L) {
+      u32x4* v = reinterpret_cast<u32x4*>(stage + (2 + bk) * BLK + p * 16);
+      *v = zero_tail(*v, key0, L);
+    }
+  }
+}
+
+// One 32-key tile of the ring.  Tiles that reach past a row's last visible key
+// (the causal tail, which covers keys past the end) exclude those keys by a
+// select on the scores; the accumulators see one code path either way.
+template <int HD>
+__device__ __forceinline__ void sk_tile(const RowCtx& r, const uint8_t* stage, int k_lds, int v_lds,
+                                        const bf16x8 (&qop)[HD / 16], float c, int kt, bool masked,
+                                        float& m_ref, float& l_run, f32x16 (&o)[HD / 32]) {
+  constexpr int KS = HD / 16;
+  constexpr int DB = HD / 32;
+  constexpr int BLK = SkTile<HD>::kBlk;
+  f32x16 x = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 kop = *reinterpret_cast<const bf16x8*>(stage + k_lds + ks * 512);
+    x = mfma32x32x16(kop, qop[ks], x);
+  }
+  if (masked) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kt + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3));
+      x[v] = key > r.vis_last ? -INFINITY : x[v];
+    }
+  }
+  float alpha;
+  bf16x8 p[2];
+  if (softmax_sub<true>(x, c, m_ref, l_run, alpha, p[0], p[1])) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const uint8_t* vb = stage + v_lds + (2 + kk) * BLK;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
+      o[db] = mfma32x32x16(vop, p[kk], o[db]);
+    }
+  }
+}
+
+// NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
+// read by that unit alone (one row tile per KV head).
+template <int HD, int NS, int WPE, bool NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void sv_attn_streamk(AttnArgs a) {
   constexpr int KS = HD / 16;
   constexpr int DB = HD / 32;
-  constexpr int BLK = LdsTile<HD>::kBlk;
-  constexpr int STAGE = LdsTile<HD>::kStage;
-  constexpr int LPB = Ring<HD>::kLoadsPerBlock;
-  constexpr int LPT = Ring<HD>::kLoadsPerTile;
+  constexpr int BLK = SkTile<HD>::kBlk;
+  constexpr int STAGE = SkTile<HD>::kStage;
+  constexpr int LPB = SkTile<HD>::kLoads;
+  static_assert(NS >= 2, "ring needs two stages");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   __shared__ int s_pref[kStreamMaxBatch + 1];
   __shared__ int s_wsum[kLdsThreads / kWave];
@@ -784,44 +955,50 @@ void sv_attn_streamk(AttnArgs a) {
   const int ql = lane & 31, hh = lane >> 5;
   const size_t blk_stride = (size_t)a.H_kv * HD * 32;
 
-  // gather offsets of this lane for the j-th 1 KB load of a block image
-  int g_k[LPB], g_v[LPB];
+  // Wave w moves block w % 2 of the tile's K (w < 2) or V (w >= 2); gather
+  // offsets of this lane for the j-th 1 KB load of the block image.
+  const bool moves_v = wave >= 2;
+  const uint8_t* src = moves_v ? a.v : a.k;
+  int g_off[LPB];
 #pragma unroll
   for (int j = 0; j < LPB; ++j) {
     const int p = j * kWave + lane;
-    g_k[j] = ((p >> 4) * 16 + swap23(p & 15)) * 16;
-    g_v[j] = ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16;
+    g_off[j] = moves_v ? ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16
+                       : ((p >> 4) * 16 + swap23(p & 15)) * 16;
   }
   const int k_lds = (ql >> 4) * BLK + (ql & 15) * 16 + hh * 256;
   const int v_lds = (2 * ql + (hh ^ vhalf_swz(ql))) * 16;
 
-  // Loads of one tile: wave w moves K and V of the tile's cache block w.
-  auto issue = [&](const Cursor& c, int stage) {
-    const int L = clamp_len(a, c.b);
-    const int n_blk = (L + 15) / 16;
-    const int32_t* tbl = a.block_table + (size_t)c.b * a.max_blocks;
+  // Table entry of the cache block this wave moves for the tile at c, read
+  // with a scalar load: vector memory operations complete in issue order, so a
+  // vector load of the entry would make its first use wait for every tile load
+  // issued before it.  Scalar loads are counted apart from them.  The entry is
+  // read one tile before its tile's loads are issued.  Entries past the
+  // sequence's last block may be read (the column is clamped to the table's
+  // width only); they only feed keys past the end, which are masked.
+  auto entry = [&](const Cursor& c) -> int {
+    const SV_CONST int32_t* tbl = (const SV_CONST int32_t*)a.block_table;
+    return tbl[(size_t)c.b * a.max_blocks + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+  };
+  // Loads of one tile into ring stage `stage`: wave w moves its block image.
+  auto issue = [&](const Cursor& c, int raw, int stage) {
     const int kvh = c.ul / a.m_tiles;
-    const size_t pb = phys_block(a, tbl, 4 * c.tile + wave, n_blk) * blk_stride + (size_t)kvh * HD * 32;
-    const uint8_t* gk = a.k + pb;
-    const uint8_t* gv = a.v + pb;
-    SV_LDS uint8_t* lk = (SV_LDS uint8_t*)(smem + stage * STAGE + wave * BLK);
-    SV_LDS uint8_t* lv = lk + 4 * BLK;
+    const uint8_t* g = src + (size_t)min(max(raw, 0), a.num_blocks - 1) * blk_stride + (size_t)kvh * HD * 32;
+    const uint32_t l = lds_addr(smem) + stage * STAGE + wave * BLK;
 #pragma unroll
-    for (int j = 0; j < LPB; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(gk + g_k[j]), (SV_LDS void*)(lk + j * 1024), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < LPB; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(gv + g_v[j]), (SV_LDS void*)(lv + j * 1024), 16, 0, 0);
+    for (int j = 0; j < LPB; ++j) dma_to_lds16<NT>(g + g_off[j], l + j * 1024);
   };
 
-  Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load
+  Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
   Cursor cc = ci;                             // tile being computed
   int gi = g0;
+  int ent = entry(ci);                        // table entry of the tile at ci
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k) {
-    issue(ci, k);
+  for (int k = 0; k < NS - 1; ++k) {         // past the range: the last tile again
+    issue(ci, ent, k);
     if (gi + 1 < g1) cursor_next(a, s_pref, ci);
     ++gi;
+    ent = entry(ci);
   }
 
   RowCtx r;
@@ -833,12 +1010,13 @@ void sv_attn_streamk(AttnArgs a) {
 
   for (int g = g0; g < g1; ++g) {
     const int t = g - g0;
-    wait_vmcnt<(NS - 2) * LPT>();
-    __builtin_amdgcn_s_barrier();
+    wait_vmcnt<(NS - 2) * LPB>();              // this wave's loads of tile g landed
+    __builtin_amdgcn_s_barrier();              // ... and every other wave's
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    issue(ci, (t + NS - 1) % NS);             // refills the stage freed by tile g - 1
+    issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
     if (gi + 1 < g1) cursor_next(a, s_pref, ci);
     ++gi;
+    ent = entry(ci);
 
     if (cc.tile == 0 || g == g0) {             // a new segment starts
       seg_start = g;
@@ -850,19 +1028,22 @@ void sv_attn_streamk(AttnArgs a) {
       r = make_row_ctx(a, 0, kvh, cc.b, L, m0, lane);
       r.k_end = L;
       if (active) load_q<HD, false>(a, r, qop);
+      // Q is waited for here, on the rare segment-start path: a wait left to its
+      // first use would sit on every tile's path and drain the ring.
+      wait_vmcnt<0>();
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = f32x16{};
       m_ref = -INFINITY;
       l_run = 0.f;
     }
-    if (active) {
-      const int kt = cc.tile * kAttnTile;
-      const uint8_t* stage = smem + (t % NS) * STAGE;
-      if (kt + kAttnTile <= r.k_end && kt + kAttnTile - 1 <= r.P)
-        ring_tile<HD, false>(r, stage, k_lds, v_lds, qop, a.c, kt, m_ref, l_run, o);
-      else
-        ring_tile<HD, true>(r, stage, k_lds, v_lds, qop, a.c, kt, m_ref, l_run, o);
+    const int kt = cc.tile * kSkKeys;
+    uint8_t* stage = smem + (t % NS) * STAGE;
+    if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
+      sk_zero_v_tail<HD>(stage, kt, r.L);
+      __syncthreads();
     }
+    if (active)                                // masked unless every key is visible to every row
+      sk_tile<HD>(r, stage, k_lds, v_lds, qop, a.c, kt, kt + kSkKeys - 1 > r.P, m_ref, l_run, o);
     if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
       if (active) {
         const bool whole = cc.tile == cc.T - 1 && seg_start == g - cc.tile;
@@ -891,7 +1072,7 @@ void sv_attn_streamk(AttnArgs a) {
     }
     if (g + 1 < g1) cursor_next(a, s_pref, cc);
   }
-  wait_vmcnt<0>();                            // drain loads issued past the range
+  wait_vmcnt<0>();                             // drain loads issued past the range
 }
 
 // Combines the segments of units that straddle range boundaries.  One wave per
@@ -1101,10 +1282,9 @@ __global__ __launch_bounds__(256) void sv_attn_combine(AttnArgs a, int total_row
 }
 
 // Stream-K variant: LDS stages per workgroup and workgroups per CU.
-constexpr int kStreamStages = SV_STREAM_STAGES;
 constexpr int kStreamWPE = SV_STREAM_WPE;
 constexpr int kStreamCUs = 256;            // MI355X compute units
-constexpr int kStreamDefaultMinTiles = 8;
+constexpr int kStreamDefaultMinKeys = 512;  // least keys per workgroup range
 
 void plan_attention(AttnPlan& p, int split_request) {
   p.G = p.H_q / p.H_kv;
@@ -1118,7 +1298,7 @@ void plan_attention(AttnPlan& p, int split_request) {
     p.split_tokens = (p.max_kv_len + kAttnTile - 1) / kAttnTile * kAttnTile;
     p.s_max = 1;
     p.sk_wgs = kStreamCUs * kStreamWPE;
-    p.min_tiles = split_request > 0 ? split_request / kAttnTile : kStreamDefaultMinTiles;
+    p.min_tiles = (split_request > 0 ? split_request : kStreamDefaultMinKeys) / kSkKeys;
     const size_t slots = (size_t)p.sk_wgs * 2 * kStreamRows;
     p.ws_meta_offset = 0;
     const size_t meta_bytes = ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256;
@@ -1153,7 +1333,12 @@ void plan_attention(AttnPlan& p, int split_request) {
 
 template <int HD>
 static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
-  sv_attn_streamk<HD, kStreamStages, kStreamWPE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+  // Row tiles of one KV head share its K/V through L2; a lone row tile reads
+  // them once, so they stream past the caches.
+  if (p.m_tiles == 1)
+    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, true><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+  else
+    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, false><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = p.B * p.H_kv * p.m_tiles;
