@@ -130,7 +130,10 @@ sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes
  *                contents on entry are ignored.
  *
  * Device preconditions: R <= kv_lens[b] <= max_kv_len; block_table[b][j] in
- * [0, num_blocks) for j < ceil(kv_lens[b] / 16) (other entries are never read);
+ * [0, num_blocks) for j < ceil(kv_lens[b] / 16).  The other entries of the
+ * table (all B x max_blocks_per_seq of which must be readable) may hold
+ * anything: they may be read, clamped into [0, num_blocks), but what they
+ * point at only meets keys past kv_lens[b], which never reach the output.
  * K and V slots past kv_lens[b] may hold anything, NaN included.
  */
 sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k_cache,

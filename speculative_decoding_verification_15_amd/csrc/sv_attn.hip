@@ -107,6 +107,14 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int b) {
   return min(max(a.kv_lens[b], 0), a.max_kv_len);
 }
 
+// The same for a wave-uniform b, read with a scalar load (no vector memory
+// counter involved).
+__device__ __forceinline__ int clamp_len_s(const AttnArgs& a, int b) {
+  const __attribute__((address_space(4))) int32_t* kl =
+      (const __attribute__((address_space(4))) int32_t*)a.kv_lens;
+  return min(max(kl[b], 0), a.max_kv_len);
+}
+
 // Work item of this workgroup.  The grid is one-dimensional and the hardware
 // hands consecutive workgroup ids to the 8 XCDs in turn, so the id is decoded
 // as (xcd = id % 8, k = id / 8): unit u = (k / m_tiles) * 8 + xcd, row tile
@@ -146,6 +154,18 @@ __device__ __forceinline__ size_t phys_block(const AttnArgs& a, const int32_t* t
 // Q^T operand: lane (row ql, half hh) supplies dims 16ks + 8hh .. +8 in k-step
 // ks (FP8_LAYOUT: the e4m3 K vector of 16 dims serves k-steps 2c and 2c + 1,
 // so half hh of k-step 2c + e holds dims 16(2c + hh) + 8e .. +8).
+// Q^T operands of the row for lanes whose row exists, and those of the row's
+// position clamp for the others (callers zero them with row_ok once the loads
+// have landed): no register is written before the loads retire.
+template <int HD>
+__device__ __forceinline__ void load_q_raw(const AttnArgs& a, const RowCtx& r,
+                                           bf16x8 (&qop)[HD / 16]) {
+  const uint16_t* qrow = a.q + ((size_t)(r.b * a.R + r.pos) * a.H_q + r.head) * HD;
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks)
+    qop[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * r.hh);
+}
+
 template <int HD, bool FP8_LAYOUT>
 __device__ __forceinline__ void load_q(const AttnArgs& a, const RowCtx& r, bf16x8 (&qop)[HD / 16]) {
   const uint16_t* qrow = a.q + ((size_t)(r.b * a.R + r.pos) * a.H_q + r.head) * HD;
@@ -229,15 +249,12 @@ __device__ __forceinline__ bool softmax_sub(const f32x16& x, float c, float& m_r
 #pragma unroll
   for (int v = 1; v < 16; ++v) hm = fmaxf(hm, x[v]);
   const float tmax = halves_max(hm * c);
-  bool move = false;
-  alpha = 1.f;
-  if (m_ref == -INFINITY) {
-    m_ref = tmax;
-  } else if (tmax > m_ref + kLazyRescale) {
-    alpha = fast_exp2(m_ref - tmax);
-    m_ref = tmax;
-    move = true;
-  }
+  // Selects rather than branches, so that the caller can overlap this VALU
+  // work with MFMAs of its own basic block.
+  const bool first = m_ref == -INFINITY;     // no visible key yet: O and l are 0
+  const bool move = !first && tmax > m_ref + kLazyRescale;
+  alpha = move ? fast_exp2(m_ref - tmax) : 1.f;
+  m_ref = (first || move) ? tmax : m_ref;
   const float m_neg = (MASKED && m_ref == -INFINITY) ? 0.f : -m_ref;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -275,6 +292,26 @@ __device__ __forceinline__ bf16x8 p_operand(const f32x16& x, int kk, float vs) {
   return p;
 }
 
+// Output row of this lane (accumulator layout: register 4 q4 + e of block db
+// holds dim 32 db + 8 q4 + 4 hh + e), times inv, as bf16.  Lanes whose row
+// does not exist must not call it.
+template <int HD>
+__device__ __forceinline__ void store_row_bf16(const AttnArgs& a, const RowCtx& r,
+                                               const f32x16 (&o)[HD / 32], float inv) {
+  uint16_t* orow = a.out + ((size_t)(r.b * a.R + r.pos) * a.H_q + r.head) * HD;
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * r.hh;
+      const uint32_t e0 = f32_to_bf16_bits(o[db][4 * q4 + 0] * inv);
+      const uint32_t e1 = f32_to_bf16_bits(o[db][4 * q4 + 1] * inv);
+      const uint32_t e2 = f32_to_bf16_bits(o[db][4 * q4 + 2] * inv);
+      const uint32_t e3 = f32_to_bf16_bits(o[db][4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(orow + d) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+    }
+}
+
 // Final division by l (single split) or the split's unnormalised state.
 template <int HD>
 __device__ __forceinline__ void write_result(const AttnArgs& a, const RowCtx& r,
@@ -284,19 +321,7 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const RowCtx& r,
   const float l_tot = halves_sum(l_run);
   if (!r.row_ok) return;
   if (r.n_splits == 1) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = a.out + ((size_t)(r.b * a.R + r.pos) * a.H_q + r.head) * HD;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * r.hh;
-        const uint32_t e0 = f32_to_bf16_bits(o[db][4 * q4 + 0] * inv);
-        const uint32_t e1 = f32_to_bf16_bits(o[db][4 * q4 + 1] * inv);
-        const uint32_t e2 = f32_to_bf16_bits(o[db][4 * q4 + 2] * inv);
-        const uint32_t e3 = f32_to_bf16_bits(o[db][4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-      }
+    store_row_bf16<HD>(a, r, o, 1.f / l_tot);
   } else {
     const size_t srow = ((size_t)(r.b * a.H_kv + r.kvh) * a.s_max + r.split) * a.M + r.m;
     float* dst = a.ws_o + srow * HD;
@@ -860,6 +885,15 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, const int* pref, 
   if (c.b < a.B) c.T = uniform((pref[c.b + 1] - pref[c.b]) / (a.H_kv * a.m_tiles));
 }
 
+// Partial O of one wave in a segment slot, in the accumulator layout: f32x4
+// number (db * 4 + q4) * 64 + lane holds registers 4 q4 .. 4 q4 + 3 of
+// accumulator block db of that lane (row 32 w + lane % 32, dims
+// 32 db + 8 q4 + 4 (lane / 32) + 0..3).
+template <int HD>
+__device__ __forceinline__ f32x4* sk_partial_o(const AttnArgs& a, int slot, int wave) {
+  return reinterpret_cast<f32x4*>(a.ws_o) + ((size_t)slot * kStreamRows + wave * kRowsPerWave) * (HD / 4);
+}
+
 // Zeroes the V values of keys >= L in the tile image at stage (keys kt ..
 // kt + 31), so that poison past the end of the sequence never meets the zero
 // probabilities of those keys in the PV product (MFMA instructions do not
@@ -879,44 +913,50 @@ __device__ __forceinline__ void sk_zero_v_tail(uint8_t* stage, int kt, int L) {
   }
 }
 
-// One 32-key tile of the ring.  Tiles that reach past a row's last visible key
-// (the causal tail, which covers keys past the end) exclude those keys by a
-// select on the scores; the accumulators see one code path either way.
+// Scores of one 32-key tile, transposed (keys x rows), from the K image of a
+// ring stage.
 template <int HD>
-__device__ __forceinline__ void sk_tile(const RowCtx& r, const uint8_t* stage, int k_lds, int v_lds,
-                                        const bf16x8 (&qop)[HD / 16], float c, int kt, bool masked,
-                                        float& m_ref, float& l_run, f32x16 (&o)[HD / 32]) {
-  constexpr int KS = HD / 16;
-  constexpr int DB = HD / 32;
-  constexpr int BLK = SkTile<HD>::kBlk;
+__device__ __forceinline__ f32x16 sk_scores(const uint8_t* stage, int k_lds,
+                                            const bf16x8 (&qop)[HD / 16]) {
   f32x16 x = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < HD / 16; ++ks) {
     const bf16x8 kop = *reinterpret_cast<const bf16x8*>(stage + k_lds + ks * 512);
     x = mfma32x32x16(kop, qop[ks], x);
   }
-  if (masked) {
+  return x;
+}
+
+// Tiles that reach past a row's last visible key (the causal tail, which
+// covers keys past the end) exclude those keys by a select on the scores.
+__device__ __forceinline__ void sk_mask(f32x16& x, const RowCtx& r, int kt) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kt + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3));
-      x[v] = key > r.vis_last ? -INFINITY : x[v];
-    }
+  for (int v = 0; v < 16; ++v) {
+    const int key = kt + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3));
+    x[v] = key > r.vis_last ? -INFINITY : x[v];
   }
-  float alpha;
-  bf16x8 p[2];
-  if (softmax_sub<true>(x, c, m_ref, l_run, alpha, p[0], p[1])) {
+}
+
+// V operands of one tile (V past the end of the sequence already zeroed).
+template <int HD>
+__device__ __forceinline__ void sk_read_v(const uint8_t* stage, int v_lds,
+                                          bf16x8 (&vop)[2][HD / 32]) {
+  constexpr int BLK = SkTile<HD>::kBlk;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-  }
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const uint8_t* vb = stage + v_lds + (2 + kk) * BLK;
+    for (int db = 0; db < HD / 32; ++db)
+      vop[kk][db] = *reinterpret_cast<const bf16x8*>(stage + v_lds + (2 + kk) * BLK + db * 1024);
+}
+
+// O += P V for one tile.
+template <int HD>
+__device__ __forceinline__ void sk_pv(const bf16x8 (&vop)[2][HD / 32], const bf16x8 (&p)[2],
+                                      f32x16 (&o)[HD / 32]) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vb + db * 1024);
-      o[db] = mfma32x32x16(vop, p[kk], o[db]);
-    }
-  }
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db) o[db] = mfma32x32x16(vop[kk][db], p[kk], o[db]);
 }
 
 // NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
@@ -930,7 +970,7 @@ void sv_attn_streamk(AttnArgs a) {
   constexpr int BLK = SkTile<HD>::kBlk;
   constexpr int STAGE = SkTile<HD>::kStage;
   constexpr int LPB = SkTile<HD>::kLoads;
-  static_assert(NS >= 2, "ring needs two stages");
+  static_assert(NS >= 3, "the ring holds the computed tile, the next one and one in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   __shared__ int s_pref[kStreamMaxBatch + 1];
   __shared__ int s_wsum[kLdsThreads / kWave];
@@ -991,6 +1031,24 @@ void sv_attn_streamk(AttnArgs a) {
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
   Cursor cc = ci;                             // tile being computed
+
+  // Row context of the segment of the tile at c; whether this wave has rows.
+  auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
+    const int kvh = c.ul / a.m_tiles;
+    const int mt = c.ul % a.m_tiles;
+    const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+    const int L = clamp_len_s(a, c.b);
+    rr = make_row_ctx(a, 0, kvh, c.b, L, m0, lane);
+    rr.k_end = L;
+    return m0 < a.M;
+  };
+  RowCtx r, rn;                                // segment of tile g; the next segment
+  bool active = seg_ctx(cc, r), active_n = false;
+  int seg_start = g0;
+  bf16x8 qop[KS], qn[KS];
+  if (active) load_q<HD, false>(a, r, qop);
+  wait_vmcnt<0>();                             // Q before the ring's loads, waited once
+
   int gi = g0;
   int ent = entry(ci);                        // table entry of the tile at ci
 #pragma unroll
@@ -1001,49 +1059,84 @@ void sv_attn_streamk(AttnArgs a) {
     ent = entry(ci);
   }
 
-  RowCtx r;
-  bool active = false;
-  int seg_start = g0;
-  bf16x8 qop[KS];
   f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  f32x16 xn;                                   // scores of tile g + 1, when have_xn
+  bool have_xn = false;
   float m_ref = -INFINITY, l_run = 0.f;
-
   for (int g = g0; g < g1; ++g) {
     const int t = g - g0;
-    wait_vmcnt<(NS - 2) * LPB>();              // this wave's loads of tile g landed
+    // This wave's loads of tiles g and g + 1 landed: loads retire in issue
+    // order, so at most tile g + 2's loads (and stores issued after them) are
+    // still counted.
+    wait_vmcnt<(NS - 3) * LPB>();
     __builtin_amdgcn_s_barrier();              // ... and every other wave's
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    if (g != g0 && cc.tile == 0) {             // a new segment, prepared one tile ago
+      seg_start = g;
+      r = rn;
+      active = active_n;
+      const bf16x8 z = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+      m_ref = -INFINITY;
+      l_run = 0.f;
+      have_xn = false;
+    }
+    // The next tile starts a segment: its row context and Q are loaded now,
+    // ahead of this tile's ring loads, so that using them next tile waits for
+    // nothing issued later.
+    if (g + 1 < g1 && cc.tile + 1 == cc.T) {
+      Cursor cn = cc;
+      cursor_next(a, s_pref, cn);
+      active_n = seg_ctx(cn, rn);
+      if (active_n) load_q_raw<HD>(a, rn, qn);
+    }
     issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
     if (gi + 1 < g1) cursor_next(a, s_pref, ci);
     ++gi;
     ent = entry(ci);
 
-    if (cc.tile == 0 || g == g0) {             // a new segment starts
-      seg_start = g;
-      const int kvh = cc.ul / a.m_tiles;
-      const int mt = cc.ul % a.m_tiles;
-      const int m0 = mt * kStreamRows + wave * kRowsPerWave;
-      active = m0 < a.M;
-      const int L = clamp_len(a, cc.b);
-      r = make_row_ctx(a, 0, kvh, cc.b, L, m0, lane);
-      r.k_end = L;
-      if (active) load_q<HD, false>(a, r, qop);
-      // Q is waited for here, on the rare segment-start path: a wait left to its
-      // first use would sit on every tile's path and drain the ring.
-      wait_vmcnt<0>();
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-      m_ref = -INFINITY;
-      l_run = 0.f;
-    }
     const int kt = cc.tile * kSkKeys;
     uint8_t* stage = smem + (t % NS) * STAGE;
     if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
       sk_zero_v_tail<HD>(stage, kt, r.L);
       __syncthreads();
     }
-    if (active)                                // masked unless every key is visible to every row
-      sk_tile<HD>(r, stage, k_lds, v_lds, qop, a.c, kt, kt + kSkKeys - 1 > r.P, m_ref, l_run, o);
+    if (active) {
+      // Software pipeline within the wave: the scores of tile g + 1 are
+      // computed (MFMA) while the softmax of tile g runs (VALU); they are kept
+      // when tile g + 1 continues this segment, which has the same Q.
+      f32x16 x = have_xn ? xn : sk_scores<HD>(stage, k_lds, qop);
+      if (kt + kSkKeys - 1 > r.P) sk_mask(x, r, kt);   // unless every key is visible to every row
+      xn = sk_scores<HD>(smem + ((t + 1) % NS) * STAGE, k_lds, qop);
+      bf16x8 vop[2][DB];
+      sk_read_v<HD>(stage, v_lds, vop);
+      float alpha;
+      bf16x8 p[2];
+      const bool rescale = softmax_sub<true>(x, a.c, m_ref, l_run, alpha, p[0], p[1]);
+      // Keep the probabilities and V operands in this block (ahead of the
+      // rescale branch), and interleave: the next tile's K reads and this
+      // tile's V reads first, then each of the next tile's score MFMAs
+      // followed by a share of this tile's softmax VALU work.
+      asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
+      __builtin_amdgcn_sched_group_barrier(0x100, KS + 2 * DB, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // ten VALU
+      }
+      if (rescale) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      sk_pv<HD>(vop, p, o);
+    }
+    have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
     if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
       if (active) {
         const bool whole = cc.tile == cc.T - 1 && seg_start == g - cc.tile;
@@ -1051,22 +1144,25 @@ void sv_attn_streamk(AttnArgs a) {
           r.n_splits = 1;
           write_result<HD>(a, r, o, m_ref, l_run);
         } else {
-          // slot 0: the range's first segment; slot 1: its last one
+          // slot 0: the range's first segment; slot 1: its last one.  O is
+          // stored in the accumulator layout (sk_partial_o), every store
+          // instruction writing 1 KB of consecutive bytes, and non-temporal:
+          // these writes land in the middle of the K/V stream, and ordinary
+          // ones cost it several times the bytes they move.
           const int slot = seg_start == g0 ? 0 : 1;
           const float l_tot = halves_sum(l_run);
-          if (r.row_ok) {
-            const size_t srow = ((size_t)blockIdx.x * 2 + slot) * kStreamRows + wave * kRowsPerWave + ql;
-            float* dst = a.ws_o + srow * HD;
+          f32x4* dst = sk_partial_o<HD>(a, (int)blockIdx.x * 2 + slot, wave) + lane;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * db + 8 * q4 + 4 * hh;
-                *reinterpret_cast<f32x4*>(dst + d) =
-                    f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]};
-              }
-            if (hh == 0) a.ws_ml[srow] = f32x2{m_ref, l_tot};
-          }
+            for (int q4 = 0; q4 < 4; ++q4)
+              __builtin_nontemporal_store(
+                  f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]},
+                  dst + (db * 4 + q4) * kWave);
+          if (hh == 0)
+            __builtin_nontemporal_store(
+                f32x2{m_ref, l_tot},
+                a.ws_ml + ((size_t)blockIdx.x * 2 + slot) * kStreamRows + wave * kRowsPerWave + ql);
         }
       }
     }
@@ -1075,24 +1171,28 @@ void sv_attn_streamk(AttnArgs a) {
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
 
-// Combines the segments of units that straddle range boundaries.  One wave per
-// (unit, row); a unit's tiles [C, C + T) were split over ranges
-// i = C / Wp .. (C + T - 1) / Wp, and range i holds its segment in slot 0 when
-// the range starts inside the unit, else (the unit began earlier) in slot 1.
+// Combines the segments of units that straddle range boundaries.  One wave
+// per (unit, 32-row block w, 32-dim block db), laid out like wave w of the
+// stream-K workgroup (lane l holds row 32 w + l % 32 in the accumulator
+// layout), so every partial-O read is 1 KB of consecutive bytes.  A unit's
+// tiles [C, C + T) were split over ranges i = C / Wp .. (C + T - 1) / Wp, and
+// range i holds its segment in slot 0 when the range starts inside the unit,
+// else (the unit began earlier) in slot 1.
 template <int HD>
-__global__ __launch_bounds__(256) void sv_attn_streamk_merge(AttnArgs a) {
-  constexpr int PER = HD / kWave;
-  constexpr int WG_PER_UNIT = kStreamRows / 4;
-  const int unit = blockIdx.x / WG_PER_UNIT;
-  const int r128 = (blockIdx.x % WG_PER_UNIT) * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
+__global__ __launch_bounds__(kWave) void sv_attn_streamk_merge(AttnArgs a) {
+  constexpr int DB = HD / 32;
+  constexpr int WAVES = kStreamRows / kRowsPerWave;
+  const int db = blockIdx.x % DB;
+  const int wave = (blockIdx.x / DB) % WAVES;
+  const int unit = blockIdx.x / (DB * WAVES);
+  const int lane = threadIdx.x;
   const int per_seq = a.H_kv * a.m_tiles;
   const int b = unit / per_seq;
   const int ul = unit % per_seq;
   const int kvh = ul / a.m_tiles;
   const int mt = ul % a.m_tiles;
-  const int m = mt * kStreamRows + r128;
-  if (b >= a.B || m >= a.M) return;
+  const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+  if (b >= a.B || m0 >= a.M) return;
   const int Wp = a.sk_meta[1];
   const int* pref = a.sk_meta + 2;
   const int T = (pref[b + 1] - pref[b]) / per_seq;
@@ -1100,33 +1200,35 @@ __global__ __launch_bounds__(256) void sv_attn_streamk_merge(AttnArgs a) {
   const int C = pref[b] + ul * T;
   const int i0 = C / Wp, i1 = (C + T - 1) / Wp;
   if (i0 == i1) return;                       // finished in place
+  const int row = wave * kRowsPerWave + lane % 32;
+  auto slot_of = [&](int i) { return i * 2 + (i * Wp >= C ? 0 : 1); };
   float mx = -INFINITY;
-  for (int i = i0; i <= i1; ++i) {
-    const int slot = i * Wp >= C ? 0 : 1;
-    mx = fmaxf(mx, a.ws_ml[((size_t)i * 2 + slot) * kStreamRows + r128][0]);
-  }
+  for (int i = i0; i <= i1; ++i)
+    mx = fmaxf(mx, a.ws_ml[(size_t)slot_of(i) * kStreamRows + row][0]);
   const float mu = (mx == -INFINITY) ? 0.f : mx;
-  float acc[PER] = {};
+  f32x4 acc[4] = {};
   float l = 0.f;
   for (int i = i0; i <= i1; ++i) {
-    const int slot = i * Wp >= C ? 0 : 1;
-    const size_t rr = ((size_t)i * 2 + slot) * kStreamRows + r128;
-    const f32x2 ml = a.ws_ml[rr];
+    const int slot = slot_of(i);
+    const f32x2 ml = a.ws_ml[(size_t)slot * kStreamRows + row];
     const float w = fast_exp2(ml[0] - mu);
     l += w * ml[1];
-    const float* src = a.ws_o + rr * HD + lane * PER;
+    const f32x4* src = sk_partial_o<HD>(a, slot, wave) + lane + db * 4 * kWave;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * src[e];
+    for (int q4 = 0; q4 < 4; ++q4) acc[q4] += w * src[q4 * kWave];
   }
+  const RowCtx r = make_row_ctx(a, 0, kvh, b, clamp_len(a, b), m0, lane);
+  if (!r.row_ok) return;
   const float inv = 1.f / l;
-  const int pos = m / a.G;
-  const int head = kvh * a.G + m % a.G;
-  uint16_t* orow = a.out + ((size_t)(b * a.R + pos) * a.H_q + head) * HD + lane * PER;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(orow) =
-        (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
-  } else {
-    orow[0] = f32_to_bf16_bits(acc[0] * inv);
+  uint16_t* orow = a.out + ((size_t)(r.b * a.R + r.pos) * a.H_q + r.head) * HD;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int d = 32 * db + 8 * q4 + 4 * r.hh;
+    const uint32_t e0 = f32_to_bf16_bits(acc[q4][0] * inv);
+    const uint32_t e1 = f32_to_bf16_bits(acc[q4][1] * inv);
+    const uint32_t e2 = f32_to_bf16_bits(acc[q4][2] * inv);
+    const uint32_t e3 = f32_to_bf16_bits(acc[q4][3] * inv);
+    *reinterpret_cast<u32x2*>(orow + d) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
   }
 }
 
@@ -1342,7 +1444,7 @@ static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = p.B * p.H_kv * p.m_tiles;
-  sv_attn_streamk_merge<HD><<<units * (kStreamRows / 4), 256, 0, stream>>>(a);
+  sv_attn_streamk_merge<HD><<<units * (kStreamRows / kRowsPerWave) * (HD / 32), kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -125,3 +125,27 @@ def test_attention_dead_tail_subblocks(name, split):
     gpu = run_attention(inp, split_tokens=split)
     assert np.isfinite(gpu).all()
     check(gpu, oracle_for(inp), f"{name}/tails/split={split}")
+
+
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_mqa_d16", "mini_fp8_d15", "mini_gqa4_d7"])
+def test_unused_table_entries_do_not_matter(name, split):
+    """Entries past a sequence's last block may be read but never reach the output."""
+    w = MINI[name]
+    L = np.array([64 * (3 + i) + rem for i, rem in enumerate(TAIL_REMAINDERS)])
+    w = w.replace(B=len(L))
+    inp = make_attn_inputs(w, T_override=L - w.R)
+    d = DeviceAttn(inp)
+    ref = d.run(split).cpu().numpy()
+    used = (inp.kv_lens.astype(np.int64) + 15) // 16
+    cols = np.arange(inp.block_table.shape[1])[None, :]
+    unused = cols >= used[:, None]
+    assert unused.any()
+    rng = np.random.default_rng(7)
+    junk = rng.choice(np.array([-(2 ** 31), 2 ** 31 - 1, -1, inp.k_cache.shape[0],
+                                inp.k_cache.shape[0] + 12345], dtype=np.int64), size=unused.sum())
+    table = inp.block_table.copy()
+    table[unused] = junk.astype(np.int32)
+    d.bt = torch.from_numpy(table).cuda()
+    got = d.run(split).cpu().numpy()
+    assert (got == ref).all()
