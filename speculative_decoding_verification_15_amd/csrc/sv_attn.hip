@@ -1391,10 +1391,13 @@ constexpr int kStreamDefaultMinKeys = 512;  // least keys per workgroup range
 void plan_attention(AttnPlan& p, int split_request) {
   p.G = p.H_q / p.H_kv;
   p.M = p.G * p.R;
+  // bf16 caches go through the stream-K ring whatever M is: units of 128 rows,
+  // waves beyond M still move their share of every tile (the K/V stream, not
+  // the MFMA work, sets the pace when few rows share a KV head).
+  p.streamk = !p.fp8 && p.B <= kStreamMaxBatch;
   const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
-  p.waves = waves_needed > 2 ? 4 : waves_needed;
+  p.waves = (waves_needed > 2 || p.streamk) ? 4 : waves_needed;
   p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);
-  p.streamk = !p.fp8 && p.waves == 4 && p.B <= kStreamMaxBatch;
   if (p.streamk) {
     // one split per unit as far as the row context goes; ranges come from min_tiles
     p.split_tokens = (p.max_kv_len + kAttnTile - 1) / kAttnTile * kAttnTile;

@@ -162,6 +162,9 @@ def test_attn_workspace_size_formula():
     slots = 512 * 2 * 128
     meta = ((4 + 3) * 4 + 255) // 256 * 256
     assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
+    # every bf16 shape takes that path, also with fewer than 128 rows per KV head
+    p = good_params(max_kv_len=1000, draft_len=3, num_q_heads=16)
+    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
 
 
 @pytest.mark.parametrize("B,D,V,status", [
