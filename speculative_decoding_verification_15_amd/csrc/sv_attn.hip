@@ -272,6 +272,43 @@ __device__ __forceinline__ bool softmax_sub(const f32x16& x, float c, float& m_r
   return __ballot(move) != 0;
 }
 
+// softmax_sub for a tile decoded from e4m3 codes: the scores of key block b
+// (16 keys: registers 8b .. 8b + 7) are scaled by cb = c * (K mantissa of
+// block b), and the probabilities of block b are returned times the block's V
+// mantissa mvb (as the PV product needs them), while l accumulates the
+// probabilities themselves.
+__device__ __forceinline__ bool softmax_sub_fp8(const f32x16& x, float c0, float c1, float mv0,
+                                                float mv1, float& m_ref, float& l_run,
+                                                float& alpha, bf16x8& p0, bf16x8& p1) {
+  float h0 = x[0], h1 = x[8];
+#pragma unroll
+  for (int v = 1; v < 8; ++v) {
+    h0 = fmaxf(h0, x[v]);
+    h1 = fmaxf(h1, x[8 + v]);
+  }
+  const float tmax = halves_max(fmaxf(h0 * c0, h1 * c1));
+  const bool first = m_ref == -INFINITY;
+  const bool move = !first && tmax > m_ref + kLazyRescale;
+  alpha = move ? fast_exp2(m_ref - tmax) : 1.f;
+  m_ref = (first || move) ? tmax : m_ref;
+  const float m_neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+  const float a0 = m_neg + __builtin_amdgcn_logf(mv0), a1 = m_neg + __builtin_amdgcn_logf(mv1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p0[j] = (__bf16)fast_exp2(__builtin_fmaf(x[j], c0, a0));
+    p1[j] = (__bf16)fast_exp2(__builtin_fmaf(x[8 + j], c1, a1));
+  }
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[j], p0[j + 1]}, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[j], p1[j + 1]}, one, s1, false);
+  }
+  l_run = l_run * alpha + s0 * __builtin_amdgcn_rcpf(mv0) + s1 * __builtin_amdgcn_rcpf(mv1);
+  return __ballot(move) != 0;
+}
+
 // Online-softmax update plus the O rescale in place (used by the direct kernel).
 template <int DB, bool MASKED>
 __device__ __forceinline__ void softmax_tile(f32x16 (&x)[2], const float (&cs)[2][2],
@@ -959,6 +996,36 @@ __device__ __forceinline__ void sk_pv(const bf16x8 (&vop)[2][HD / 32], const bf1
     for (int db = 0; db < HD / 32; ++db) o[db] = mfma32x32x16(vop[kk][db], p[kk], o[db]);
 }
 
+// Ends a segment of a stream-K range: the unit's output rows when the segment
+// covers the whole unit, else the unnormalised (O, m, l) in segment slot
+// `slot` (the range's first segment or its last one).  O is stored in the
+// accumulator layout (sk_partial_o), every store instruction writing 1 KB of
+// consecutive bytes, and non-temporal: these writes land in the middle of the
+// K/V stream, and ordinary ones cost it several times the bytes they move.
+template <int HD>
+__device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
+                                               const f32x16 (&o)[HD / 32], float m_ref,
+                                               float l_run, bool whole, int slot, int wave,
+                                               int lane) {
+  if (whole) {
+    r.n_splits = 1;
+    write_result<HD>(a, r, o, m_ref, l_run);
+    return;
+  }
+  const float l_tot = halves_sum(l_run);
+  f32x4* dst = sk_partial_o<HD>(a, slot, wave) + lane;
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      __builtin_nontemporal_store(
+          f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]},
+          dst + (db * 4 + q4) * kWave);
+  if (lane < 32)
+    __builtin_nontemporal_store(f32x2{m_ref, l_tot},
+                                a.ws_ml + (size_t)slot * kStreamRows + wave * kRowsPerWave + lane);
+}
+
 // NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
 // read by that unit alone (one row tile per KV head).
 template <int HD, int NS, int WPE, bool NT>
@@ -1138,33 +1205,245 @@ void sv_attn_streamk(AttnArgs a) {
     }
     have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
     if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
-      if (active) {
-        const bool whole = cc.tile == cc.T - 1 && seg_start == g - cc.tile;
-        if (whole) {
-          r.n_splits = 1;
-          write_result<HD>(a, r, o, m_ref, l_run);
-        } else {
-          // slot 0: the range's first segment; slot 1: its last one.  O is
-          // stored in the accumulator layout (sk_partial_o), every store
-          // instruction writing 1 KB of consecutive bytes, and non-temporal:
-          // these writes land in the middle of the K/V stream, and ordinary
-          // ones cost it several times the bytes they move.
-          const int slot = seg_start == g0 ? 0 : 1;
-          const float l_tot = halves_sum(l_run);
-          f32x4* dst = sk_partial_o<HD>(a, (int)blockIdx.x * 2 + slot, wave) + lane;
+      if (active)
+        sk_segment_end<HD>(a, r, o, m_ref, l_run,
+                           cc.tile == cc.T - 1 && seg_start == g - cc.tile,
+                           (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
+    }
+    if (g + 1 < g1) cursor_next(a, s_pref, cc);
+  }
+  wait_vmcnt<0>();                             // drain loads issued past the range
+}
+
+// Stream-K kernel for e4m3 caches.  The same work list, ranges, segments and
+// merge as the bf16 kernel; what differs is the tile supply.  A 16-key block
+// of e4m3 K or V is hd x 16 codes (half the bf16 bytes): the codes of NS8
+// tiles stream through a DMA ring, and at every tile each wave decodes the
+// block it moved for the next tile -- codes times the block's scale, rounded
+// once to bf16 -- into one of two bf16 images laid out like a bf16 ring
+// stage (V past the end of the sequence zeroed), on which the tile is then
+// computed exactly as in the bf16 kernel.
+template <int HD>
+struct SkTile8 {
+  static constexpr int kBlk = HD * 16;       // bytes of one block of e4m3 K or V
+  static constexpr int kStage = 4 * kBlk;    // K blocks 0, 1, then V blocks 0, 1
+  static constexpr int kLoads = kBlk / 1024; // 1 KB wave loads per block
+  static constexpr int kStages = 4;
+};
+
+template <int HD, int WPE, bool NT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
+                          amdgpu_waves_per_eu(WPE, WPE)))
+void sv_attn_streamk_fp8(AttnArgs a) {
+  constexpr int KS = HD / 16;
+  constexpr int DB = HD / 32;
+  constexpr int BLK = SkTile<HD>::kBlk;      // bf16 image
+  constexpr int STAGE = SkTile<HD>::kStage;
+  constexpr int BLK8 = SkTile8<HD>::kBlk;    // e4m3 ring
+  constexpr int STAGE8 = SkTile8<HD>::kStage;
+  constexpr int LPB = SkTile8<HD>::kLoads;
+  constexpr int NS8 = SkTile8<HD>::kStages;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring8[NS8 * STAGE8];
+  __shared__ __attribute__((aligned(1024))) uint8_t img[2 * STAGE];
+  __shared__ f32x4 s_mant[2];                 // per image: mantissas of K0, K1, V0, V1 scales
+  __shared__ int s_pref[kStreamMaxBatch + 1];
+  __shared__ int s_wsum[kLdsThreads / kWave];
+
+  build_prefix(a, s_pref, s_wsum);
+  const int W = uniform(s_pref[a.B]);
+  const int Wp = max((W + (int)gridDim.x - 1) / (int)gridDim.x, a.min_tiles);
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    for (int b = tid; b <= a.B; b += kLdsThreads) a.sk_meta[2 + b] = s_pref[b];
+    if (tid == 0) {
+      a.sk_meta[0] = W;
+      a.sk_meta[1] = Wp;
+    }
+  }
+  const int g0 = (int)blockIdx.x * Wp;
+  const int g1 = min(g0 + Wp, W);
+  if (g0 >= g1) return;                       // whole workgroup, after the last barrier use
+
+  const int wave = uniform(tid / kWave);
+  const int lane = tid % kWave;
+  const int ql = lane & 31, hh = lane >> 5;
+  const size_t blk_stride = (size_t)a.H_kv * BLK8;
+
+  // Wave w moves (and decodes) block w % 2 of the tile's K (w < 2) or V (w >= 2).
+  const bool moves_v = wave >= 2;
+  const uint8_t* src = moves_v ? a.v : a.k;
+  const SV_CONST float* scales = (const SV_CONST float*)(moves_v ? a.v_scale : a.k_scale);
+  const int k_lds = (ql >> 4) * BLK + (ql & 15) * 16 + hh * 256;
+  const int v_lds = (2 * ql + (hh ^ vhalf_swz(ql))) * 16;
+
+  // Table entry of this wave's block of the tile at c (a scalar load, as in
+  // the bf16 kernel; entries past the sequence's last block may be read).
+  auto entry = [&](const Cursor& c) -> int {
+    const SV_CONST int32_t* tbl = (const SV_CONST int32_t*)a.block_table;
+    return tbl[(size_t)c.b * a.max_blocks + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+  };
+  // Codes of one tile into ring stage `stage` (linear copy of the block); the
+  // block's scale is returned (a scalar load, first used a tile later).
+  auto issue = [&](const Cursor& c, int raw, int stage) -> float {
+    const int kvh = c.ul / a.m_tiles;
+    const size_t pb = (size_t)min(max(raw, 0), a.num_blocks - 1);
+    const uint8_t* g = src + pb * blk_stride + (size_t)kvh * BLK8;
+    const uint32_t l = lds_addr(ring8) + stage * STAGE8 + wave * BLK8;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+    for (int j = 0; j < LPB; ++j) dma_to_lds16<NT>(g + (j * kWave + lane) * 16, l + j * 1024);
+    return scales[pb * a.H_kv + kvh];
+  };
+  // Decoding this wave's block of a tile: the codes of ring stage `stage`
+  // (read first, so that the conversion can overlap MFMA work), then their
+  // bf16 values into image `im`.  V past the end of the sequence is zeroed
+  // later, on the image, for the sequence's last tile only.
+  auto dec_read = [&](int stage, u32x4 (&raw)[LPB]) {
+    const uint8_t* s8 = ring8 + stage * STAGE8 + wave * BLK8;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              __builtin_nontemporal_store(
-                  f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]},
-                  dst + (db * 4 + q4) * kWave);
-          if (hh == 0)
-            __builtin_nontemporal_store(
-                f32x2{m_ref, l_tot},
-                a.ws_ml + ((size_t)blockIdx.x * 2 + slot) * kStreamRows + wave * kRowsPerWave + ql);
-        }
+    for (int j = 0; j < LPB; ++j) raw[j] = *reinterpret_cast<const u32x4*>(s8 + (j * kWave + lane) * 16);
+  };
+  // Image offsets of the two bf16 vectors each code vector becomes (K: 16
+  // dims of key slot p % 16; V: 16 key slots of dim p), fixed per lane.
+  int off_lo[LPB], off_hi[LPB];
+#pragma unroll
+  for (int j = 0; j < LPB; ++j) {
+    const int p = j * kWave + lane;
+    const int k_off = ((2 * (p >> 4)) * 16 + swap23(p & 15)) * 16;
+    off_lo[j] = wave * BLK + (moves_v ? (2 * p + vhalf_swz(p)) * 16 : k_off);
+    off_hi[j] = wave * BLK + (moves_v ? (2 * p + (1 ^ vhalf_swz(p))) * 16 : k_off + 256);
+  }
+  auto dec_write = [&](const u32x4 (&raw)[LPB], int im, float scale) {
+    uint8_t* dst = img + im * STAGE;             // K blocks 0, 1 then V blocks 0, 1
+    float pow2, mant;
+    split_scale(scale, pow2, mant);
+#pragma unroll
+    for (int j = 0; j < LPB; ++j) {
+      u32x4 lo, hi;
+      e4m3x16_pow2_bf16(raw[j], pow2, lo, hi);
+      *reinterpret_cast<u32x4*>(dst + off_lo[j]) = lo;
+      *reinterpret_cast<u32x4*>(dst + off_hi[j]) = hi;
+    }
+    if (lane == 0) reinterpret_cast<float*>(&s_mant[im])[wave] = mant;
+  };
+
+  Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
+  Cursor cc = ci;                             // tile being computed
+  auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
+    const int kvh = c.ul / a.m_tiles;
+    const int mt = c.ul % a.m_tiles;
+    const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+    const int L = clamp_len_s(a, c.b);
+    rr = make_row_ctx(a, 0, kvh, c.b, L, m0, lane);
+    rr.k_end = L;
+    return m0 < a.M;
+  };
+  RowCtx r, rn;                                // segment of tile g; the next segment
+  bool active = seg_ctx(cc, r), active_n = false;
+  int seg_start = g0;
+  bf16x8 qop[KS], qn[KS];
+  if (active) load_q<HD, false>(a, r, qop);
+  wait_vmcnt<0>();                             // Q before the ring's loads, waited once
+
+  // Tiles g0 .. g0 + NS8 - 1 in flight; sq holds the scales of the tiles
+  // loaded but not yet decoded, oldest first.
+  int gi = g0;
+  int ent = entry(ci);
+  float sq[NS8];
+#pragma unroll
+  for (int k = 0; k < NS8; ++k) {            // past the range: the last tile again
+    sq[k] = issue(ci, ent, k);
+    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    ++gi;
+    ent = entry(ci);
+  }
+  wait_vmcnt<(NS8 - 1) * LPB>();             // this wave's codes of tile g0
+  {
+    u32x4 raw[LPB];
+    dec_read(0, raw);
+    dec_write(raw, 0, sq[0]);
+  }
+#pragma unroll
+  for (int k = 0; k + 1 < NS8; ++k) sq[k] = sq[k + 1];
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  for (int g = g0; g < g1; ++g) {
+    const int t = g - g0;
+    // this wave's codes of tile g + 1 landed (tiles g + 2 .. g + NS8 - 1 may
+    // not have: loads retire in issue order)
+    wait_vmcnt<(NS8 - 2) * LPB>();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();              // image t % 2 complete; image (t + 1) % 2 free
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    if (g != g0 && cc.tile == 0) {             // a new segment, prepared one tile ago
+      seg_start = g;
+      r = rn;
+      active = active_n;
+      const bf16x8 z = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+      m_ref = -INFINITY;
+      l_run = 0.f;
+    }
+    const bool next_in_unit = cc.tile + 1 < cc.T;
+    if (g + 1 < g1 && !next_in_unit) {         // the next tile starts a segment
+      Cursor cn = cc;
+      cursor_next(a, s_pref, cn);
+      active_n = seg_ctx(cn, rn);
+      if (active_n) load_q_raw<HD>(a, rn, qn);
+    }
+    // Tile g + 1 is decoded during this tile's compute (past the range the
+    // stage holds the last tile again: decoded, never used).
+    const float dec_scale = sq[0];
+#pragma unroll
+    for (int k = 0; k + 2 < NS8; ++k) sq[k] = sq[k + 1];
+    sq[NS8 - 2] = issue(ci, ent, t % NS8);     // refills the stage decoded last tile
+    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    ++gi;
+    ent = entry(ci);
+
+    const int kt = cc.tile * kSkKeys;
+    uint8_t* im = img + (t & 1) * STAGE;
+    if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
+      sk_zero_v_tail<HD>(im, kt, r.L);
+      __syncthreads();
+    }
+    u32x4 raw[LPB];
+    dec_read((t + 1) % NS8, raw);
+    if (active) {
+      f32x16 x = sk_scores<HD>(im, k_lds, qop);
+      dec_write(raw, (t + 1) & 1, dec_scale);
+      // the score MFMAs, each followed by a share of the decoding VALU work
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);          // DS reads
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6 * LPB, 0);   // VALU
       }
+      if (kt + kSkKeys - 1 > r.P) sk_mask(x, r, kt);   // unless every key is visible to every row
+      bf16x8 vop[2][DB];
+      sk_read_v<HD>(im, v_lds, vop);
+      const f32x4 mt4 = s_mant[t & 1];
+      float alpha;
+      bf16x8 p[2];
+      if (softmax_sub_fp8(x, a.c * mt4[0], a.c * mt4[1], mt4[2], mt4[3], m_ref, l_run, alpha, p[0], p[1])) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      sk_pv<HD>(vop, p, o);
+    } else {
+      dec_write(raw, (t + 1) & 1, dec_scale);
+    }
+    if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
+      if (active)
+        sk_segment_end<HD>(a, r, o, m_ref, l_run,
+                           cc.tile == cc.T - 1 && seg_start == g - cc.tile,
+                           (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
     if (g + 1 < g1) cursor_next(a, s_pref, cc);
   }
@@ -1394,7 +1673,7 @@ void plan_attention(AttnPlan& p, int split_request) {
   // bf16 caches go through the stream-K ring whatever M is: units of 128 rows,
   // waves beyond M still move their share of every tile (the K/V stream, not
   // the MFMA work, sets the pace when few rows share a KV head).
-  p.streamk = !p.fp8 && p.B <= kStreamMaxBatch;
+  p.streamk = p.B <= kStreamMaxBatch;
   const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
   p.waves = (waves_needed > 2 || p.streamk) ? 4 : waves_needed;
   p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);
@@ -1440,7 +1719,11 @@ template <int HD>
 static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
   // Row tiles of one KV head share its K/V through L2; a lone row tile reads
   // them once, so they stream past the caches.
-  if (p.m_tiles == 1)
+  if (p.fp8 && p.m_tiles == 1)
+    sv_attn_streamk_fp8<HD, kStreamWPE, true><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+  else if (p.fp8)
+    sv_attn_streamk_fp8<HD, kStreamWPE, false><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+  else if (p.m_tiles == 1)
     sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, true><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else
     sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, false><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);

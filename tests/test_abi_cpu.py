@@ -147,12 +147,12 @@ def test_attn_fp8_needs_scales_and_workspace_size():
 
 
 def test_attn_workspace_size_formula():
-    # split-K path (e4m3 cache): one split needs no workspace
-    p = good_params(max_kv_len=1000, split_tokens=1024, kv_dtype=sv.SV_KV_FP8_E4M3)
+    # split-K path (batches above 2048): one split needs no workspace
+    p = good_params(batch=2049, max_kv_len=1000, split_tokens=1024, kv_dtype=sv.SV_KV_FP8_E4M3)
     assert sv.spec_verify_attn_workspace_size(p) == 0
     # four splits of 256 keys: O (hd floats) and (m, l) per split and query row
-    p = good_params(max_kv_len=1000, split_tokens=256, kv_dtype=sv.SV_KV_FP8_E4M3)
-    B, H_kv, S, M, hd = 4, 8, 4, 8 * 16, 128
+    p = good_params(batch=2049, max_kv_len=1000, split_tokens=256)
+    B, H_kv, S, M, hd = 2049, 8, 4, 8 * 16, 128
     rows = B * H_kv * S * M
     o_bytes = rows * hd * 4
     assert sv.spec_verify_attn_workspace_size(p) == (o_bytes + 255) // 256 * 256 + rows * 8
@@ -162,8 +162,11 @@ def test_attn_workspace_size_formula():
     slots = 512 * 2 * 128
     meta = ((4 + 3) * 4 + 255) // 256 * 256
     assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
-    # every bf16 shape takes that path, also with fewer than 128 rows per KV head
+    # every shape with B <= 2048 takes that path: fewer than 128 rows per KV
+    # head, e4m3 caches
     p = good_params(max_kv_len=1000, draft_len=3, num_q_heads=16)
+    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
+    p = good_params(max_kv_len=1000, kv_dtype=sv.SV_KV_FP8_E4M3)
     assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
 
 
