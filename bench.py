@@ -75,6 +75,15 @@ def attn_algorithmic_flops(inp) -> int:
     return int(inp.kv_lens.astype(np.int64).sum()) * w.H_kv * 4 * w.M * w.hd
 
 
+def attn_kernel_names(w) -> str:
+    """The kernels one spec_verify_attn launch runs for this workload (batches
+    up to 2048 take the stream-K path)."""
+    if w.B > 2048:
+        return "spec_verify_attn (split-K partial kernel + sv_attn_combine)"
+    main = "sv_attn_streamk_fp8" if w.kv_dtype == "fp8_e4m3" else "sv_attn_streamk"
+    return f"spec_verify_attn ({main} + sv_attn_streamk_merge)"
+
+
 def read_traffic(src_hash):
     """HBM traffic per attention launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
@@ -251,7 +260,7 @@ def main():
             "split_tokens": int(p.split_tokens) or "auto",
             "logit_buffers_rotated": n_sets, "parallelism": "single GPU"},
         "roofline": {
-            "kernel": "spec_verify_attn (sv_attn_partial + sv_attn_combine)",
+            "kernel": attn_kernel_names(w),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(attn_us, 2)},
