@@ -8,7 +8,7 @@
 // section "Basic structure of speculative decoding": AL in 1 .. 1 + D).
 //
 // Pass 1 (sv_argmax_partial) streams the logits once: every workgroup reduces a
-// chunk of 8192 logits of one row to (max value, lowest index holding it).
+// chunk of 4096 logits of one row to (max value, lowest index holding it).
 // Pass 2 (sv_accept_finalize) reduces the chunk results of each row and runs
 // the prefix scan for one sequence per wave.  Ties resolve to the lower index
 // everywhere; values are compared as floats, never as bit patterns, so -0 and

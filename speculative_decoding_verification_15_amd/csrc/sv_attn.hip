@@ -836,11 +836,11 @@ void sv_attn_partial_ring(AttnArgs a) {
 // Every workgroup computes the per-sequence tile prefix from kv_lens in LDS;
 // workgroup 0 also stores it (with W and Wp) for the merge kernel.
 //
-// A tile is one 32-key sub-block (16 KB of K and V at hd 128), so the 64 KB
-// ring of each of the two workgroups on a compute unit holds four stages and
-// keeps three tiles of loads in flight while one is computed: at the HBM
-// latency it is the bytes in flight, not the issue rate, that bound the
-// bandwidth a workgroup draws.
+// A tile is one 32-key sub-block (16 KB of K and V at hd 128); the 64 KB ring
+// of each of the two workgroups on a compute unit holds four stages: the tile
+// being computed, the next one (whose scores are computed early) and two in
+// flight.  (A fifth stage, which LDS would allow now that the prefix table
+// lives in the ring, measured no faster.)
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxBatch = 2048;
 constexpr int kStreamRows = 128;          // rows per unit (4 waves x 32)
@@ -911,15 +911,22 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, const int* pref, 
   return c;
 }
 
-__device__ __forceinline__ void cursor_next(const AttnArgs& a, const int* pref, Cursor& c) {
+// Tiles of each unit of sequence b (the per-sequence count build_prefix sums).
+__device__ __forceinline__ int unit_tiles(const AttnArgs& a, int b) {
+  return (clamp_len_s(a, b) + kSkKeys - 1) / kSkKeys;
+}
+
+// Advances to the next tile of the work list.  The tile count of a new
+// sequence comes from kv_lens (a scalar load, once per sequence), so the
+// prefix table is needed only to place a range's first tile.
+__device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   if (++c.tile < c.T) return;
   c.tile = 0;
   if (++c.ul < a.H_kv * a.m_tiles) return;
   c.ul = 0;
   do {
     ++c.b;
-  } while (c.b < a.B && uniform(pref[c.b + 1]) == uniform(pref[c.b]));
-  if (c.b < a.B) c.T = uniform((pref[c.b + 1] - pref[c.b]) / (a.H_kv * a.m_tiles));
+  } while (c.b < a.B && (c.T = unit_tiles(a, c.b)) == 0);
 }
 
 // Partial O of one wave in a segment slot, in the accumulator layout: f32x4
@@ -1039,8 +1046,11 @@ void sv_attn_streamk(AttnArgs a) {
   constexpr int LPB = SkTile<HD>::kLoads;
   static_assert(NS >= 3, "the ring holds the computed tile, the next one and one in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-  __shared__ int s_pref[kStreamMaxBatch + 1];
-  __shared__ int s_wsum[kLdsThreads / kWave];
+  // The prefix table only places the range's first tile: it lives in the ring
+  // until the ring's first loads are issued.
+  static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= NS * STAGE, "prefix table fits");
+  int* s_pref = reinterpret_cast<int*>(smem);
+  int* s_wsum = s_pref + kStreamMaxBatch + 1;
 
   build_prefix(a, s_pref, s_wsum);
   const int W = uniform(s_pref[a.B]);
@@ -1098,6 +1108,7 @@ void sv_attn_streamk(AttnArgs a) {
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
   Cursor cc = ci;                             // tile being computed
+  __syncthreads();                            // the prefix table is dead: the ring may fill
 
   // Row context of the segment of the tile at c; whether this wave has rows.
   auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
@@ -1121,7 +1132,7 @@ void sv_attn_streamk(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {         // past the range: the last tile again
     issue(ci, ent, k);
-    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    if (gi + 1 < g1) cursor_next(a, ci);
     ++gi;
     ent = entry(ci);
   }
@@ -1159,12 +1170,12 @@ void sv_attn_streamk(AttnArgs a) {
     // nothing issued later.
     if (g + 1 < g1 && cc.tile + 1 == cc.T) {
       Cursor cn = cc;
-      cursor_next(a, s_pref, cn);
+      cursor_next(a, cn);
       active_n = seg_ctx(cn, rn);
       if (active_n) load_q_raw<HD>(a, rn, qn);
     }
     issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
-    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    if (gi + 1 < g1) cursor_next(a, ci);
     ++gi;
     ent = entry(ci);
 
@@ -1210,7 +1221,7 @@ void sv_attn_streamk(AttnArgs a) {
                            cc.tile == cc.T - 1 && seg_start == g - cc.tile,
                            (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
-    if (g + 1 < g1) cursor_next(a, s_pref, cc);
+    if (g + 1 < g1) cursor_next(a, cc);
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
@@ -1246,8 +1257,10 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring8[NS8 * STAGE8];
   __shared__ __attribute__((aligned(1024))) uint8_t img[2 * STAGE];
   __shared__ f32x4 s_mant[2];                 // per image: mantissas of K0, K1, V0, V1 scales
-  __shared__ int s_pref[kStreamMaxBatch + 1];
-  __shared__ int s_wsum[kLdsThreads / kWave];
+  // the prefix table lives in the images until the first tile is decoded
+  static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= 2 * STAGE, "prefix table fits");
+  int* s_pref = reinterpret_cast<int*>(img);
+  int* s_wsum = s_pref + kStreamMaxBatch + 1;
 
   build_prefix(a, s_pref, s_wsum);
   const int W = uniform(s_pref[a.B]);
@@ -1328,6 +1341,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
   Cursor cc = ci;                             // tile being computed
+  __syncthreads();                            // the prefix table is dead: images may be written
   auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
     const int kvh = c.ul / a.m_tiles;
     const int mt = c.ul % a.m_tiles;
@@ -1352,7 +1366,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < NS8; ++k) {            // past the range: the last tile again
     sq[k] = issue(ci, ent, k);
-    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    if (gi + 1 < g1) cursor_next(a, ci);
     ++gi;
     ent = entry(ci);
   }
@@ -1393,7 +1407,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     const bool next_in_unit = cc.tile + 1 < cc.T;
     if (g + 1 < g1 && !next_in_unit) {         // the next tile starts a segment
       Cursor cn = cc;
-      cursor_next(a, s_pref, cn);
+      cursor_next(a, cn);
       active_n = seg_ctx(cn, rn);
       if (active_n) load_q_raw<HD>(a, rn, qn);
     }
@@ -1403,7 +1417,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k + 2 < NS8; ++k) sq[k] = sq[k + 1];
     sq[NS8 - 2] = issue(ci, ent, t % NS8);     // refills the stage decoded last tile
-    if (gi + 1 < g1) cursor_next(a, s_pref, ci);
+    if (gi + 1 < g1) cursor_next(a, ci);
     ++gi;
     ent = entry(ci);
 
@@ -1445,7 +1459,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
                            cc.tile == cc.T - 1 && seg_start == g - cc.tile,
                            (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
-    if (g + 1 < g1) cursor_next(a, s_pref, cc);
+    if (g + 1 < g1) cursor_next(a, cc);
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }

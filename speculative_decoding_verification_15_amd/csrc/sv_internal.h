@@ -48,7 +48,7 @@ void plan_attention(AttnPlan& plan, int split_tokens_request);
 hipError_t launch_attention(const AttnPlan& plan, const AttnPtrs& ptrs, hipStream_t stream);
 
 constexpr int kArgmaxThreads = 256;
-constexpr int kArgmaxChunk = kArgmaxThreads * 4 * 8;  // logits per workgroup
+constexpr int kArgmaxChunk = kArgmaxThreads * 4 * 4;  // logits per workgroup
 
 inline int argmax_chunks(int vocab) { return (vocab + kArgmaxChunk - 1) / kArgmaxChunk; }
 inline size_t accept_workspace_bytes(int B, int D, int V) {

@@ -207,7 +207,7 @@ def test_accept_pointer_errors():
 
 @pytest.mark.parametrize("B,D,V", [(1, 0, 1), (4, 3, 1024), (32, 15, 128256), (3, 63, 8193)])
 def test_accept_workspace_size(B, D, V):
-    chunks = -(-V // 8192)
+    chunks = -(-V // 4096)
     assert sv.spec_accept_workspace_size(B, D, V) == B * (D + 1) * chunks * 8
 
 
