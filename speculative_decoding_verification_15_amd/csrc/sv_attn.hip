@@ -1239,7 +1239,7 @@ struct SkTile8 {
   static constexpr int kBlk = HD * 16;       // bytes of one block of e4m3 K or V
   static constexpr int kStage = 4 * kBlk;    // K blocks 0, 1, then V blocks 0, 1
   static constexpr int kLoads = kBlk / 1024; // 1 KB wave loads per block
-  static constexpr int kStages = 4;
+  static constexpr int kStages = 3;
 };
 
 template <int HD, int WPE, bool NT>
@@ -1255,10 +1255,11 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   constexpr int LPB = SkTile8<HD>::kLoads;
   constexpr int NS8 = SkTile8<HD>::kStages;
   __shared__ __attribute__((aligned(1024))) uint8_t ring8[NS8 * STAGE8];
-  __shared__ __attribute__((aligned(1024))) uint8_t img[2 * STAGE];
-  __shared__ f32x4 s_mant[2];                 // per image: mantissas of K0, K1, V0, V1 scales
+  __shared__ __attribute__((aligned(1024))) uint8_t img[3 * STAGE];
+  __shared__ f32x4 s_mant[3];                 // per image: mantissas of K0, K1, V0, V1 scales
   // the prefix table lives in the images until the first tile is decoded
-  static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= 2 * STAGE, "prefix table fits");
+  static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= 3 * STAGE, "prefix table fits");
+  static_assert(NS8 == 3, "the prologue below fills a three-stage code ring");
   int* s_pref = reinterpret_cast<int*>(img);
   int* s_wsum = s_pref + kStreamMaxBatch + 1;
 
@@ -1358,38 +1359,51 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   if (active) load_q<HD, false>(a, r, qop);
   wait_vmcnt<0>();                             // Q before the ring's loads, waited once
 
-  // Tiles g0 .. g0 + NS8 - 1 in flight; sq holds the scales of the tiles
-  // loaded but not yet decoded, oldest first.
+  // Tile t of the range (t = g - g0) is decoded into image t % 3 two tiles
+  // ahead of its computation; its scores are computed (MFMA) one tile ahead,
+  // under the softmax of the tile before it, as in the bf16 kernel.  sq holds
+  // the scales of the tiles loaded but not yet decoded, oldest first.
   int gi = g0;
   int ent = entry(ci);
   float sq[NS8];
-#pragma unroll
-  for (int k = 0; k < NS8; ++k) {            // past the range: the last tile again
-    sq[k] = issue(ci, ent, k);
+  auto load_next = [&](int stage) -> float {  // past the range: the last tile again
+    const float sc = issue(ci, ent, stage);
     if (gi + 1 < g1) cursor_next(a, ci);
     ++gi;
     ent = entry(ci);
-  }
-  wait_vmcnt<(NS8 - 1) * LPB>();             // this wave's codes of tile g0
-  {
+    return sc;
+  };
+  auto decode_now = [&](int stage, int im, float scale) {
     u32x4 raw[LPB];
-    dec_read(0, raw);
-    dec_write(raw, 0, sq[0]);
-  }
+    dec_read(stage, raw);
+    dec_write(raw, im, scale);
+  };
 #pragma unroll
-  for (int k = 0; k + 1 < NS8; ++k) sq[k] = sq[k + 1];
+  for (int k = 0; k < NS8; ++k) sq[k] = load_next(k);   // tiles 0, 1, 2
+  wait_vmcnt<2 * LPB>();                       // this wave's codes of tile 0
+  decode_now(0, 0, sq[0]);
+  sq[0] = sq[1];
+  sq[1] = sq[2];
+  sq[2] = load_next(0);                        // tile 3
+  wait_vmcnt<2 * LPB>();                       // ... of tile 1
+  decode_now(1, 1, sq[0]);
+  sq[0] = sq[1];
+  sq[1] = sq[2];
+  sq[2] = load_next(1);                        // tile 4
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  f32x16 xn;                                   // scores of tile g + 1, when have_xn
+  bool have_xn = false;
   float m_ref = -INFINITY, l_run = 0.f;
   for (int g = g0; g < g1; ++g) {
     const int t = g - g0;
-    // this wave's codes of tile g + 1 landed (tiles g + 2 .. g + NS8 - 1 may
-    // not have: loads retire in issue order)
-    wait_vmcnt<(NS8 - 2) * LPB>();
+    // this wave's codes of tile g + 2 landed (tiles g + 3, g + 4 may not have:
+    // loads retire in issue order)
+    wait_vmcnt<2 * LPB>();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();              // image t % 2 complete; image (t + 1) % 2 free
+    __builtin_amdgcn_s_barrier();              // images of tiles g, g + 1 complete; tile g - 1's free
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
     if (g != g0 && cc.tile == 0) {             // a new segment, prepared one tile ago
@@ -1403,56 +1417,61 @@ void sv_attn_streamk_fp8(AttnArgs a) {
       for (int db = 0; db < DB; ++db) o[db] = f32x16{};
       m_ref = -INFINITY;
       l_run = 0.f;
+      have_xn = false;
     }
-    const bool next_in_unit = cc.tile + 1 < cc.T;
-    if (g + 1 < g1 && !next_in_unit) {         // the next tile starts a segment
+    if (g + 1 < g1 && cc.tile + 1 == cc.T) {   // the next tile starts a segment
       Cursor cn = cc;
       cursor_next(a, cn);
       active_n = seg_ctx(cn, rn);
       if (active_n) load_q_raw<HD>(a, rn, qn);
     }
-    // Tile g + 1 is decoded during this tile's compute (past the range the
-    // stage holds the last tile again: decoded, never used).
-    const float dec_scale = sq[0];
-#pragma unroll
-    for (int k = 0; k + 2 < NS8; ++k) sq[k] = sq[k + 1];
-    sq[NS8 - 2] = issue(ci, ent, t % NS8);     // refills the stage decoded last tile
-    if (gi + 1 < g1) cursor_next(a, ci);
-    ++gi;
-    ent = entry(ci);
+    // codes of tile g + 2 (decoded in this tile's compute block; past the
+    // range the stage holds the last tile again: decoded, never used)
+    const int dstage = (t + 2) % NS8, dimg = (t + 2) % 3;
+    u32x4 raw[LPB];
+    dec_read(dstage, raw);
+    const float dscale = sq[0];
 
     const int kt = cc.tile * kSkKeys;
-    uint8_t* im = img + (t & 1) * STAGE;
+    uint8_t* im = img + (t % 3) * STAGE;
     if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
       sk_zero_v_tail<HD>(im, kt, r.L);
       __syncthreads();
     }
-    u32x4 raw[LPB];
-    dec_read((t + 1) % NS8, raw);
     if (active) {
-      f32x16 x = sk_scores<HD>(im, k_lds, qop);
-      dec_write(raw, (t + 1) & 1, dec_scale);
-      // the score MFMAs, each followed by a share of the decoding VALU work
-      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);          // DS reads
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6 * LPB, 0);   // VALU
-      }
+      f32x16 x = have_xn ? xn : sk_scores<HD>(im, k_lds, qop);
       if (kt + kSkKeys - 1 > r.P) sk_mask(x, r, kt);   // unless every key is visible to every row
-      bf16x8 vop[2][DB];
-      sk_read_v<HD>(im, v_lds, vop);
-      const f32x4 mt4 = s_mant[t & 1];
+      xn = sk_scores<HD>(img + ((t + 1) % 3) * STAGE, k_lds, qop);
+      const f32x4 mt4 = s_mant[t % 3];
       float alpha;
       bf16x8 p[2];
-      if (softmax_sub_fp8(x, a.c * mt4[0], a.c * mt4[1], mt4[2], mt4[3], m_ref, l_run, alpha, p[0], p[1])) {
+      const bool rescale = softmax_sub_fp8(x, a.c * mt4[0], a.c * mt4[1], mt4[2], mt4[3], m_ref,
+                                           l_run, alpha, p[0], p[1]);
+      dec_write(raw, dimg, dscale);
+      // probabilities and the decode stay ahead of the rescale branch; the
+      // next tile's score MFMAs interleave with the VALU work
+      asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);           // DS reads
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);         // VALU
+      }
+      if (rescale) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
       }
+      bf16x8 vop[2][DB];
+      sk_read_v<HD>(im, v_lds, vop);
       sk_pv<HD>(vop, p, o);
     } else {
-      dec_write(raw, (t + 1) & 1, dec_scale);
+      dec_write(raw, dimg, dscale);
     }
+    have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
+    // refill the stage just decoded (its codes were consumed above)
+    sq[0] = sq[1];
+    sq[1] = sq[2];
+    sq[2] = load_next(dstage);
     if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
       if (active)
         sk_segment_end<HD>(a, r, o, m_ref, l_run,
