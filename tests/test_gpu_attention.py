@@ -17,7 +17,8 @@ import torch
 from oracle.attention import oracle_attn
 from tests.gpu_util import (MAX_ABS_TOL, MEAN_ABS_TOL, DeviceAttn, attn_errors, note,
                             run_attention)
-from workloads import (EDGE, FP8_LONG, LLAMA3_8B, LLAMA31_70B, MINI, SWEEP_D, TINY,
+from workloads import (EDGE, FP8_LONG, KV_BF16, KV_FP8, LLAMA3_8B, LLAMA31_70B, MINI, SWEEP_D, TINY,
+                       Workload,
                        make_attn_inputs, tile_sweep)
 
 pytestmark = pytest.mark.gpu
@@ -149,3 +150,39 @@ def test_unused_table_entries_do_not_matter(name, split):
     d.bt = torch.from_numpy(table).cuda()
     got = d.run(split).cpu().numpy()
     assert (got == ref).all()
+
+
+def _sampled_check(inp, label, n_rand=6):
+    gpu = run_attention(inp)
+    assert np.isfinite(gpu).all(), "a row is not finite"
+    L = inp.kv_lens
+    rng = np.random.default_rng(11)
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, inp.w.B - 1}
+                  | set(rng.integers(0, inp.w.B, n_rand).tolist()))
+    check(gpu, oracle_for(inp, seqs=seqs), label)
+
+
+# More than 2048 sequences take the split-K path (partial kernels + combine):
+# M = 16 rows per KV head runs the direct kernel, M = 128 the LDS ring (bf16)
+# or the register-staged kernel (e4m3).  Contexts start at 32 tokens: with
+# only a handful of keys an output row is hardly an average (|O| near 3), and
+# its bf16 rounding alone would use most of the 1e-2 bar.
+@pytest.mark.parametrize("kv", [KV_BF16, KV_FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("G,D", [(4, 3), (8, 15)], ids=["m16", "m128"])
+def test_split_path_above_2048_sequences(kv, G, D):
+    w = Workload(f"batch2100_{kv}_g{G}_d{D}", 3001, B=2100, H_q=2 * G, H_kv=2, hd=64, D=D,
+                 T_range=(32, 90), kv_dtype=kv)
+    _sampled_check(make_attn_inputs(w), w.name)
+
+
+# Many short sequences on the stream-K path: most 32-key tiles start or end a
+# segment, whole units finish inside ranges, and ranges cut units of two tiles
+# (contexts from 32 tokens, as above).
+@pytest.mark.parametrize("kv", [KV_BF16, KV_FP8], ids=["bf16", "fp8"])
+def test_streamk_many_short_sequences(kv):
+    w = Workload(f"short1500_{kv}", 3002, B=1500, H_q=16, H_kv=2, hd=128, D=15,
+                 T_range=(32, 150), kv_dtype=kv)
+    inp = make_attn_inputs(w)
+    gpu = run_attention(inp)
+    assert np.isfinite(gpu).all()
+    check(gpu, oracle_for(inp), w.name)
