@@ -888,9 +888,13 @@ __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* 
 }
 
 // Position in the work list: sequence b, unit ul = kvh * m_tiles + mt within
-// the sequence, tile within the unit, and the unit's tile count T.
+// the sequence, tile within the unit, and the unit's tile count T; kvh, mt and
+// the offset of sequence b's block-table row are kept alongside, so that the
+// per-tile path does no division or wide multiply.
 struct Cursor {
   int b, ul, tile, T;
+  int kvh, mt;
+  size_t row;
 };
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -908,6 +912,9 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, const int* pref, 
   const int r = g - uniform(pref[lo]);
   c.ul = r / c.T;
   c.tile = r % c.T;
+  c.kvh = c.ul / a.m_tiles;
+  c.mt = c.ul % a.m_tiles;
+  c.row = (size_t)c.b * a.max_blocks;
   return c;
 }
 
@@ -922,11 +929,18 @@ __device__ __forceinline__ int unit_tiles(const AttnArgs& a, int b) {
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   if (++c.tile < c.T) return;
   c.tile = 0;
-  if (++c.ul < a.H_kv * a.m_tiles) return;
+  ++c.ul;
+  if (++c.mt == a.m_tiles) {
+    c.mt = 0;
+    ++c.kvh;
+  }
+  if (c.ul < a.H_kv * a.m_tiles) return;
   c.ul = 0;
+  c.kvh = 0;
   do {
     ++c.b;
   } while (c.b < a.B && (c.T = unit_tiles(a, c.b)) == 0);
+  c.row = (size_t)c.b * a.max_blocks;
 }
 
 // Partial O of one wave in a segment slot, in the accumulator layout: f32x4
@@ -1095,12 +1109,11 @@ void sv_attn_streamk(AttnArgs a) {
   // width only); they only feed keys past the end, which are masked.
   auto entry = [&](const Cursor& c) -> int {
     const SV_CONST int32_t* tbl = (const SV_CONST int32_t*)a.block_table;
-    return tbl[(size_t)c.b * a.max_blocks + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+    return tbl[c.row + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
   };
   // Loads of one tile into ring stage `stage`: wave w moves its block image.
   auto issue = [&](const Cursor& c, int raw, int stage) {
-    const int kvh = c.ul / a.m_tiles;
-    const uint8_t* g = src + (size_t)min(max(raw, 0), a.num_blocks - 1) * blk_stride + (size_t)kvh * HD * 32;
+    const uint8_t* g = src + (size_t)min(max(raw, 0), a.num_blocks - 1) * blk_stride + (size_t)c.kvh * HD * 32;
     const uint32_t l = lds_addr(smem) + stage * STAGE + wave * BLK;
 #pragma unroll
     for (int j = 0; j < LPB; ++j) dma_to_lds16<NT>(g + g_off[j], l + j * 1024);
@@ -1112,11 +1125,9 @@ void sv_attn_streamk(AttnArgs a) {
 
   // Row context of the segment of the tile at c; whether this wave has rows.
   auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
-    const int kvh = c.ul / a.m_tiles;
-    const int mt = c.ul % a.m_tiles;
-    const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+    const int m0 = c.mt * kStreamRows + wave * kRowsPerWave;
     const int L = clamp_len_s(a, c.b);
-    rr = make_row_ctx(a, 0, kvh, c.b, L, m0, lane);
+    rr = make_row_ctx(a, 0, c.kvh, c.b, L, m0, lane);
     rr.k_end = L;
     return m0 < a.M;
   };
@@ -1294,18 +1305,17 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   // the bf16 kernel; entries past the sequence's last block may be read).
   auto entry = [&](const Cursor& c) -> int {
     const SV_CONST int32_t* tbl = (const SV_CONST int32_t*)a.block_table;
-    return tbl[(size_t)c.b * a.max_blocks + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+    return tbl[c.row + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
   };
   // Codes of one tile into ring stage `stage` (linear copy of the block); the
   // block's scale is returned (a scalar load, first used a tile later).
   auto issue = [&](const Cursor& c, int raw, int stage) -> float {
-    const int kvh = c.ul / a.m_tiles;
     const size_t pb = (size_t)min(max(raw, 0), a.num_blocks - 1);
-    const uint8_t* g = src + pb * blk_stride + (size_t)kvh * BLK8;
+    const uint8_t* g = src + pb * blk_stride + (size_t)c.kvh * BLK8;
     const uint32_t l = lds_addr(ring8) + stage * STAGE8 + wave * BLK8;
 #pragma unroll
     for (int j = 0; j < LPB; ++j) dma_to_lds16<NT>(g + (j * kWave + lane) * 16, l + j * 1024);
-    return scales[pb * a.H_kv + kvh];
+    return scales[pb * a.H_kv + c.kvh];
   };
   // Decoding this wave's block of a tile: the codes of ring stage `stage`
   // (read first, so that the conversion can overlap MFMA work), then their
@@ -1344,11 +1354,9 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   Cursor cc = ci;                             // tile being computed
   __syncthreads();                            // the prefix table is dead: images may be written
   auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
-    const int kvh = c.ul / a.m_tiles;
-    const int mt = c.ul % a.m_tiles;
-    const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+    const int m0 = c.mt * kStreamRows + wave * kRowsPerWave;
     const int L = clamp_len_s(a, c.b);
-    rr = make_row_ctx(a, 0, kvh, c.b, L, m0, lane);
+    rr = make_row_ctx(a, 0, c.kvh, c.b, L, m0, lane);
     rr.k_end = L;
     return m0 < a.M;
   };
