@@ -894,7 +894,7 @@ __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* 
 struct Cursor {
   int b, ul, tile, T;
   int kvh, mt;
-  size_t row;
+  const int32_t* row;
 };
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -914,7 +914,7 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, const int* pref, 
   c.tile = r % c.T;
   c.kvh = c.ul / a.m_tiles;
   c.mt = c.ul % a.m_tiles;
-  c.row = (size_t)c.b * a.max_blocks;
+  c.row = a.block_table + (size_t)c.b * a.max_blocks;
   return c;
 }
 
@@ -940,7 +940,7 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   do {
     ++c.b;
   } while (c.b < a.B && (c.T = unit_tiles(a, c.b)) == 0);
-  c.row = (size_t)c.b * a.max_blocks;
+  c.row = a.block_table + (size_t)c.b * a.max_blocks;
 }
 
 // Partial O of one wave in a segment slot, in the accumulator layout: f32x4
@@ -1108,8 +1108,8 @@ void sv_attn_streamk(AttnArgs a) {
   // sequence's last block may be read (the column is clamped to the table's
   // width only); they only feed keys past the end, which are masked.
   auto entry = [&](const Cursor& c) -> int {
-    const SV_CONST int32_t* tbl = (const SV_CONST int32_t*)a.block_table;
-    return tbl[c.row + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+    const SV_CONST int32_t* row = (const SV_CONST int32_t*)c.row;
+    return row[(unsigned)min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
   };
   // Loads of one tile into ring stage `stage`: wave w moves its block image.
   auto issue = [&](const Cursor& c, int raw, int stage) {
@@ -1155,7 +1155,7 @@ void sv_attn_streamk(AttnArgs a) {
   bool have_xn = false;
   float m_ref = -INFINITY, l_run = 0.f;
   for (int g = g0; g < g1; ++g) {
-    const int t = g - g0;
+    const unsigned t = (unsigned)(g - g0);    // unsigned: stage indices are cheap remainders
     // This wave's loads of tiles g and g + 1 landed: loads retire in issue
     // order, so at most tile g + 2's loads (and stores issued after them) are
     // still counted.
@@ -1304,8 +1304,8 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   // Table entry of this wave's block of the tile at c (a scalar load, as in
   // the bf16 kernel; entries past the sequence's last block may be read).
   auto entry = [&](const Cursor& c) -> int {
-    const SV_CONST int32_t* tbl = (const SV_CONST int32_t*)a.block_table;
-    return tbl[c.row + min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+    const SV_CONST int32_t* row = (const SV_CONST int32_t*)c.row;
+    return row[(unsigned)min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
   };
   // Codes of one tile into ring stage `stage` (linear copy of the block); the
   // block's scale is returned (a scalar load, first used a tile later).
@@ -1406,7 +1406,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   bool have_xn = false;
   float m_ref = -INFINITY, l_run = 0.f;
   for (int g = g0; g < g1; ++g) {
-    const int t = g - g0;
+    const unsigned t = (unsigned)(g - g0);    // unsigned: stage indices are cheap remainders
     // this wave's codes of tile g + 2 landed (tiles g + 3, g + 4 may not have:
     // loads retire in issue order)
     wait_vmcnt<2 * LPB>();
