@@ -62,6 +62,7 @@ struct AttnArgs {
   int min_tiles;  // stream-K: least tiles per workgroup
   float c;        // sm_scale * log2(e)
   int* sk_meta;   // stream-K: [W, Wp, pref[0..B]] written by workgroup 0 for the merge
+  int sk_rows;    // stream-K: rows per unit (128 or 256)
 };
 
 // Row i of the 32-key score block holds key pi(i) of that block.
@@ -843,7 +844,7 @@ void sv_attn_partial_ring(AttnArgs a) {
 // lives in the ring, measured no faster.)
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxBatch = 2048;
-constexpr int kStreamRows = 128;          // rows per unit (4 waves x 32)
+constexpr int kStreamRows = 128;          // rows per unit of 4 waves x 32 (8-wave units: 256)
 constexpr int kSkKeys = 32;               // keys per stream-K tile
 
 #ifndef SV_STREAM_RING_BYTES
@@ -856,6 +857,7 @@ struct SkTile {
   static constexpr int kStage = 4 * kBlk;          // K blocks 0, 1, then V blocks 0, 1
   static constexpr int kLoads = kBlk / 1024;       // 1 KB wave loads per block
   static constexpr int kStages = SV_STREAM_RING_BYTES / kStage;
+  static constexpr int kStages8 = 2 * SV_STREAM_RING_BYTES / kStage;   // one 8-wave workgroup per CU
 };
 
 // pref[b] = tiles of all units of sequences before b, for b = 0 .. B.
@@ -863,7 +865,8 @@ __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
   const int per_seq = a.H_kv * a.m_tiles;
-  const int chunk = (a.B + kLdsThreads - 1) / kLdsThreads;
+  const int nthreads = (int)blockDim.x;
+  const int chunk = (a.B + nthreads - 1) / nthreads;
   const int lo = min(tid * chunk, a.B), hi = min(lo + chunk, a.B);
   int sum = 0;
   for (int b = lo; b < hi; ++b) {
@@ -949,7 +952,7 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
 // 32 db + 8 q4 + 4 (lane / 32) + 0..3).
 template <int HD>
 __device__ __forceinline__ f32x4* sk_partial_o(const AttnArgs& a, int slot, int wave) {
-  return reinterpret_cast<f32x4*>(a.ws_o) + ((size_t)slot * kStreamRows + wave * kRowsPerWave) * (HD / 4);
+  return reinterpret_cast<f32x4*>(a.ws_o) + ((size_t)slot * a.sk_rows + wave * kRowsPerWave) * (HD / 4);
 }
 
 // Zeroes the V values of keys >= L in the tile image at stage (keys kt ..
@@ -960,7 +963,7 @@ template <int HD>
 __device__ __forceinline__ void sk_zero_v_tail(uint8_t* stage, int kt, int L) {
   constexpr int BLK = SkTile<HD>::kBlk;
   constexpr int POS = 2 * HD;                // 16-byte vectors per V block image
-  for (int i = threadIdx.x; i < 2 * POS; i += kLdsThreads) {
+  for (int i = threadIdx.x; i < 2 * POS; i += blockDim.x) {
     const int bk = i / POS, p = i % POS;
     const int d = p >> 1, h = (p & 1) ^ vhalf_swz(d);
     const int key0 = kt + 16 * bk + 8 * h;
@@ -1044,13 +1047,15 @@ __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
           dst + (db * 4 + q4) * kWave);
   if (lane < 32)
     __builtin_nontemporal_store(f32x2{m_ref, l_tot},
-                                a.ws_ml + (size_t)slot * kStreamRows + wave * kRowsPerWave + lane);
+                                a.ws_ml + (size_t)slot * a.sk_rows + wave * kRowsPerWave + lane);
 }
 
 // NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
-// read by that unit alone (one row tile per KV head).
-template <int HD, int NS, int WPE, bool NT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
+// read by that unit alone (one row tile per KV head).  WAVES = 4 (units of 128
+// rows, two workgroups per CU) or 8 (units of 256 rows, one per CU), so that
+// up to 256 rows of one KV head stream its K and V once.
+template <int HD, int NS, int WPE, bool NT, int WAVES>
+__global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void sv_attn_streamk(AttnArgs a) {
   constexpr int KS = HD / 16;
@@ -1062,7 +1067,11 @@ void sv_attn_streamk(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   // The prefix table only places the range's first tile: it lives in the ring
   // until the ring's first loads are issued.
-  static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= NS * STAGE, "prefix table fits");
+  constexpr int ROWS = WAVES * kRowsPerWave;
+  constexpr int WPB = WAVES / 4;               // waves sharing one block image of a tile
+  constexpr int LPW = LPB / WPB;               // 1 KB loads per wave per tile
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+  static_assert((kStreamMaxBatch + 1 + WAVES) * 4 <= NS * STAGE, "prefix table fits");
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_wsum = s_pref + kStreamMaxBatch + 1;
 
@@ -1071,7 +1080,7 @@ void sv_attn_streamk(AttnArgs a) {
   const int Wp = max((W + (int)gridDim.x - 1) / (int)gridDim.x, a.min_tiles);
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
-    for (int b = tid; b <= a.B; b += kLdsThreads) a.sk_meta[2 + b] = s_pref[b];
+    for (int b = tid; b <= a.B; b += WAVES * kWave) a.sk_meta[2 + b] = s_pref[b];
     if (tid == 0) {
       a.sk_meta[0] = W;
       a.sk_meta[1] = Wp;
@@ -1086,14 +1095,17 @@ void sv_attn_streamk(AttnArgs a) {
   const int ql = lane & 31, hh = lane >> 5;
   const size_t blk_stride = (size_t)a.H_kv * HD * 32;
 
-  // Wave w moves block w % 2 of the tile's K (w < 2) or V (w >= 2); gather
-  // offsets of this lane for the j-th 1 KB load of the block image.
-  const bool moves_v = wave >= 2;
+  // Wave w moves 1 KB chunks j0 .. j0 + LPW - 1 of block image bw of every
+  // tile (bw: K block 0, K block 1, V block 0, V block 1); gather offsets of
+  // this lane for each of its loads.
+  const int bw = wave / WPB;
+  const int j0 = (wave % WPB) * LPW;
+  const bool moves_v = bw >= 2;
   const uint8_t* src = moves_v ? a.v : a.k;
-  int g_off[LPB];
+  int g_off[LPW];
 #pragma unroll
-  for (int j = 0; j < LPB; ++j) {
-    const int p = j * kWave + lane;
+  for (int j = 0; j < LPW; ++j) {
+    const int p = (j0 + j) * kWave + lane;
     g_off[j] = moves_v ? ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16
                        : ((p >> 4) * 16 + swap23(p & 15)) * 16;
   }
@@ -1109,14 +1121,14 @@ void sv_attn_streamk(AttnArgs a) {
   // width only); they only feed keys past the end, which are masked.
   auto entry = [&](const Cursor& c) -> int {
     const SV_CONST int32_t* row = (const SV_CONST int32_t*)c.row;
-    return row[(unsigned)min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+    return row[(unsigned)min(2 * c.tile + (bw & 1), a.max_blocks - 1)];
   };
-  // Loads of one tile into ring stage `stage`: wave w moves its block image.
+  // Loads of one tile into ring stage `stage`: this wave's chunks of block bw.
   auto issue = [&](const Cursor& c, int raw, int stage) {
     const uint8_t* g = src + (size_t)min(max(raw, 0), a.num_blocks - 1) * blk_stride + (size_t)c.kvh * HD * 32;
-    const uint32_t l = lds_addr(smem) + stage * STAGE + wave * BLK;
+    const uint32_t l = lds_addr(smem) + stage * STAGE + bw * BLK + j0 * 1024;
 #pragma unroll
-    for (int j = 0; j < LPB; ++j) dma_to_lds16<NT>(g + g_off[j], l + j * 1024);
+    for (int j = 0; j < LPW; ++j) dma_to_lds16<NT>(g + g_off[j], l + j * 1024);
   };
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
@@ -1125,7 +1137,7 @@ void sv_attn_streamk(AttnArgs a) {
 
   // Row context of the segment of the tile at c; whether this wave has rows.
   auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
-    const int m0 = c.mt * kStreamRows + wave * kRowsPerWave;
+    const int m0 = c.mt * ROWS + wave * kRowsPerWave;
     const int L = clamp_len_s(a, c.b);
     rr = make_row_ctx(a, 0, c.kvh, c.b, L, m0, lane);
     rr.k_end = L;
@@ -1159,7 +1171,7 @@ void sv_attn_streamk(AttnArgs a) {
     // This wave's loads of tiles g and g + 1 landed: loads retire in issue
     // order, so at most tile g + 2's loads (and stores issued after them) are
     // still counted.
-    wait_vmcnt<(NS - 3) * LPB>();
+    wait_vmcnt<(NS - 3) * LPW>();
     __builtin_amdgcn_s_barrier();              // ... and every other wave's
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
@@ -1501,17 +1513,17 @@ void sv_attn_streamk_fp8(AttnArgs a) {
 template <int HD>
 __global__ __launch_bounds__(kWave) void sv_attn_streamk_merge(AttnArgs a) {
   constexpr int DB = HD / 32;
-  constexpr int WAVES = kStreamRows / kRowsPerWave;
+  const int waves = a.sk_rows / kRowsPerWave;
   const int db = blockIdx.x % DB;
-  const int wave = (blockIdx.x / DB) % WAVES;
-  const int unit = blockIdx.x / (DB * WAVES);
+  const int wave = (blockIdx.x / DB) % waves;
+  const int unit = blockIdx.x / (DB * waves);
   const int lane = threadIdx.x;
   const int per_seq = a.H_kv * a.m_tiles;
   const int b = unit / per_seq;
   const int ul = unit % per_seq;
   const int kvh = ul / a.m_tiles;
   const int mt = ul % a.m_tiles;
-  const int m0 = mt * kStreamRows + wave * kRowsPerWave;
+  const int m0 = mt * a.sk_rows + wave * kRowsPerWave;
   if (b >= a.B || m0 >= a.M) return;
   const int Wp = a.sk_meta[1];
   const int* pref = a.sk_meta + 2;
@@ -1524,13 +1536,13 @@ __global__ __launch_bounds__(kWave) void sv_attn_streamk_merge(AttnArgs a) {
   auto slot_of = [&](int i) { return i * 2 + (i * Wp >= C ? 0 : 1); };
   float mx = -INFINITY;
   for (int i = i0; i <= i1; ++i)
-    mx = fmaxf(mx, a.ws_ml[(size_t)slot_of(i) * kStreamRows + row][0]);
+    mx = fmaxf(mx, a.ws_ml[(size_t)slot_of(i) * a.sk_rows + row][0]);
   const float mu = (mx == -INFINITY) ? 0.f : mx;
   f32x4 acc[4] = {};
   float l = 0.f;
   for (int i = i0; i <= i1; ++i) {
     const int slot = slot_of(i);
-    const f32x2 ml = a.ws_ml[(size_t)slot * kStreamRows + row];
+    const f32x2 ml = a.ws_ml[(size_t)slot * a.sk_rows + row];
     const float w = fast_exp2(ml[0] - mu);
     l += w * ml[1];
     const f32x4* src = sk_partial_o<HD>(a, slot, wave) + lane + db * 4 * kWave;
@@ -1709,22 +1721,33 @@ constexpr int kStreamCUs = 256;            // MI355X compute units
 constexpr int kStreamDefaultMinKeys = 512;  // least keys per workgroup range
 
 void plan_attention(AttnPlan& p, int split_request) {
+  p.sk_rows = 0;
+  p.sk_wgs = 0;
   p.G = p.H_q / p.H_kv;
   p.M = p.G * p.R;
-  // bf16 caches go through the stream-K ring whatever M is: units of 128 rows,
+  // Batches up to kStreamMaxBatch go through the stream-K ring whatever M is:
   // waves beyond M still move their share of every tile (the K/V stream, not
-  // the MFMA work, sets the pace when few rows share a KV head).
+  // the MFMA work, sets the pace when few rows share a KV head).  bf16 units
+  // hold 128 rows (4 waves, two workgroups per CU) or, for 129 .. 256 rows per
+  // KV head, 256 rows (8 waves, one workgroup per CU), so that those rows
+  // stream their K and V once instead of twice.  Beyond 256 rows (MQA-like
+  // heads) the row tiles of a KV head share its K/V through L2 and two 4-wave
+  // workgroups per CU hide latency better (measured); e4m3 units hold 128.
   p.streamk = p.B <= kStreamMaxBatch;
   const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
-  p.waves = (waves_needed > 2 || p.streamk) ? 4 : waves_needed;
+  if (p.streamk)
+    p.waves = (!p.fp8 && p.M > kStreamRows && p.M <= 2 * kStreamRows) ? 8 : 4;
+  else
+    p.waves = waves_needed > 2 ? 4 : waves_needed;
   p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);
   if (p.streamk) {
     // one split per unit as far as the row context goes; ranges come from min_tiles
     p.split_tokens = (p.max_kv_len + kAttnTile - 1) / kAttnTile * kAttnTile;
     p.s_max = 1;
-    p.sk_wgs = kStreamCUs * kStreamWPE;
+    p.sk_rows = p.waves * kRowsPerWave;
+    p.sk_wgs = p.waves == 8 ? kStreamCUs : kStreamCUs * kStreamWPE;
     p.min_tiles = (split_request > 0 ? split_request : kStreamDefaultMinKeys) / kSkKeys;
-    const size_t slots = (size_t)p.sk_wgs * 2 * kStreamRows;
+    const size_t slots = (size_t)p.sk_wgs * 2 * p.sk_rows;
     p.ws_meta_offset = 0;
     const size_t meta_bytes = ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256;
     p.ws_o_bytes = slots * p.hd * sizeof(float);
@@ -1764,14 +1787,18 @@ static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream
     sv_attn_streamk_fp8<HD, kStreamWPE, true><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.fp8)
     sv_attn_streamk_fp8<HD, kStreamWPE, false><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+  else if (p.waves == 8 && p.m_tiles == 1)
+    sv_attn_streamk<HD, SkTile<HD>::kStages8, 2, true, 8><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
+  else if (p.waves == 8)
+    sv_attn_streamk<HD, SkTile<HD>::kStages8, 2, false, 8><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
   else if (p.m_tiles == 1)
-    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, true><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, true, 4><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else
-    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, false><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, false, 4><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = p.B * p.H_kv * p.m_tiles;
-  sv_attn_streamk_merge<HD><<<units * (kStreamRows / kRowsPerWave) * (HD / 32), kWave, 0, stream>>>(a);
+  sv_attn_streamk_merge<HD><<<units * (p.sk_rows / kRowsPerWave) * (HD / 32), kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1828,6 +1855,7 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   }
   a.ws_ml = p.ws_bytes ? reinterpret_cast<f32x2*>(ws + p.ws_ml_offset) : nullptr;
   a.min_tiles = p.min_tiles;
+  a.sk_rows = p.sk_rows;
   a.B = p.B;
   a.R = p.R;
   a.H_q = p.H_q;

@@ -27,6 +27,7 @@ struct AttnPlan {
   // number of 64-key tiles per workgroup, and the metadata block in the workspace
   bool streamk;
   int sk_wgs, min_tiles;
+  int sk_rows;       // rows per stream-K unit: 32 per wave, 4 or 8 waves
   size_t ws_meta_offset;
   size_t ws_o_bytes, ws_ml_offset, ws_bytes;
 };
