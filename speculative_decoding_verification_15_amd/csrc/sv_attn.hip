@@ -1348,6 +1348,9 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     off_lo[j] = wave * BLK + (moves_v ? (2 * p + vhalf_swz(p)) * 16 : k_off);
     off_hi[j] = wave * BLK + (moves_v ? (2 * p + (1 ^ vhalf_swz(p))) * 16 : k_off + 256);
   }
+  // The scale's power of two goes into the conversion; its mantissa is kept
+  // for the softmax (put_mant, a store by one lane: kept out of the compute
+  // block, whose instruction schedule a branch would split).
   auto dec_write = [&](const u32x4 (&raw)[LPB], int im, float scale) {
     uint8_t* dst = img + im * STAGE;             // K blocks 0, 1 then V blocks 0, 1
     float pow2, mant;
@@ -1359,6 +1362,10 @@ void sv_attn_streamk_fp8(AttnArgs a) {
       *reinterpret_cast<u32x4*>(dst + off_lo[j]) = lo;
       *reinterpret_cast<u32x4*>(dst + off_hi[j]) = hi;
     }
+  };
+  auto put_mant = [&](int im, float scale) {
+    float pow2, mant;
+    split_scale(scale, pow2, mant);
     if (lane == 0) reinterpret_cast<float*>(&s_mant[im])[wave] = mant;
   };
 
@@ -1397,6 +1404,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     u32x4 raw[LPB];
     dec_read(stage, raw);
     dec_write(raw, im, scale);
+    put_mant(im, scale);
   };
 #pragma unroll
   for (int k = 0; k < NS8; ++k) sq[k] = load_next(k);   // tiles 0, 1, 2
@@ -1451,6 +1459,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     u32x4 raw[LPB];
     dec_read(dstage, raw);
     const float dscale = sq[0];
+    put_mant(dimg, dscale);                    // tile g - 1, the image's last user, is done
 
     const int kt = cc.tile * kSkKeys;
     uint8_t* im = img + (t % 3) * STAGE;
@@ -1481,9 +1490,12 @@ void sv_attn_streamk_fp8(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
       }
+      // V reads all issued ahead of the PV MFMAs (the score operands are dead)
       bf16x8 vop[2][DB];
       sk_read_v<HD>(im, v_lds, vop);
       sk_pv<HD>(vop, p, o);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);       // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);       // MFMA
     } else {
       dec_write(raw, dimg, dscale);
     }
