@@ -129,6 +129,10 @@ sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes
  *                bytes (may be NULL when that size is 0), 256-byte aligned;
  *                contents on entry are ignored.
  *
+ * Size limits (SV_ERR_UNSUPPORTED beyond them): B*R*H_q*hd < 2^31 elements;
+ * H_kv*hd*32 < 2^31 (bytes of one physical block of a bf16 cache, all KV
+ * heads); num_blocks*H_kv < 2^32 (entries of a scale array).
+ *
  * Device preconditions: R <= kv_lens[b] <= max_kv_len; block_table[b][j] in
  * [0, num_blocks) for j < ceil(kv_lens[b] / 16).  The other entries of the
  * table (all B x max_blocks_per_seq of which must be readable) may hold

@@ -62,6 +62,11 @@ sv_status make_attn_plan(const sv_attn_params* p, sv::AttnPlan& plan) {
   // index arithmetic inside the kernels uses 32-bit row counts
   const long long q_elems = (long long)p->batch * R * p->num_q_heads * p->head_dim;
   if (q_elems >= (1LL << 31)) return fail(SV_ERR_UNSUPPORTED, "q/out larger than 2^31 elements");
+  // ... and 32-bit block strides and scale indices
+  if ((long long)p->num_kv_heads * p->head_dim * 32 >= (1LL << 31))
+    return fail(SV_ERR_UNSUPPORTED, "a cache block of num_kv_heads * head_dim * 32 bytes is 2^31 or more");
+  if ((long long)p->num_blocks * p->num_kv_heads >= (1LL << 32))
+    return fail(SV_ERR_UNSUPPORTED, "num_blocks * num_kv_heads must be below 2^32");
 
   plan = sv::AttnPlan{};
   plan.B = p->batch;

@@ -656,6 +656,31 @@ __device__ __forceinline__ void dma_to_lds16(const void* src, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// N such loads of consecutive 1 KB pieces: piece j of the wave's source (src +
+// 1024 j + 16 i for lane i) lands at lds + 1024 j + 16 i.  One M0 value serves
+// all of them: the instruction's immediate offset is added to both the global
+// and the LDS address.
+#define SV_DMA1(off, nt) "\n\tglobal_load_lds_dwordx4 %0, off offset:" #off nt
+template <bool NT, int N>
+__device__ __forceinline__ void dma_to_lds16_run(const void* src, uint32_t lds) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 pieces");
+  if constexpr (NT && N == 4)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0" SV_DMA1(0, " nt") SV_DMA1(1024, " nt")
+                 SV_DMA1(2048, " nt") SV_DMA1(3072, " nt") : : "v"(src), "s"(lds) : "memory", "m0");
+  else if constexpr (N == 4)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0" SV_DMA1(0, "") SV_DMA1(1024, "")
+                 SV_DMA1(2048, "") SV_DMA1(3072, "") : : "v"(src), "s"(lds) : "memory", "m0");
+  else if constexpr (NT && N == 2)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0" SV_DMA1(0, " nt") SV_DMA1(1024, " nt")
+                 : : "v"(src), "s"(lds) : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0" SV_DMA1(0, "") SV_DMA1(1024, "")
+                 : : "v"(src), "s"(lds) : "memory", "m0");
+  else
+    dma_to_lds16<NT>(src, lds);
+}
+#undef SV_DMA1
+
 // One 64-key tile of the bf16 LDS image.  Masked tiles (the causal tail or the
 // end of the sequence) run every MFMA like unmasked ones: keys past the end are
 // excluded by selects on the scores and their V values are zeroed by selects,
@@ -1100,15 +1125,15 @@ void sv_attn_streamk(AttnArgs a) {
   // this lane for each of its loads.
   const int bw = wave / WPB;
   const int j0 = (wave % WPB) * LPW;
+  // The permutations act within 1 KB pieces (K: 16-byte vectors within 256
+  // bytes; V: the two halves of a key pair, chosen by key bits 2 and 3), so
+  // chunk j starts 1 KB after chunk 0 and one offset serves all of them.
   const bool moves_v = bw >= 2;
   const uint8_t* src = moves_v ? a.v : a.k;
-  int g_off[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int p = (j0 + j) * kWave + lane;
-    g_off[j] = moves_v ? ((p >> 1) * 2 + ((p & 1) ^ vhalf_swz(p >> 1))) * 16
-                       : ((p >> 4) * 16 + swap23(p & 15)) * 16;
-  }
+  const uint32_t blk_stride32 = (uint32_t)blk_stride;   // below 2^32 (the planner checks)
+  const int p0 = j0 * kWave + lane;
+  const int g_off = moves_v ? ((p0 >> 1) * 2 + ((p0 & 1) ^ vhalf_swz(p0 >> 1))) * 16
+                            : ((p0 >> 4) * 16 + swap23(p0 & 15)) * 16;
   const int k_lds = (ql >> 4) * BLK + (ql & 15) * 16 + hh * 256;
   const int v_lds = (2 * ql + (hh ^ vhalf_swz(ql))) * 16;
 
@@ -1125,10 +1150,10 @@ void sv_attn_streamk(AttnArgs a) {
   };
   // Loads of one tile into ring stage `stage`: this wave's chunks of block bw.
   auto issue = [&](const Cursor& c, int raw, int stage) {
-    const uint8_t* g = src + (size_t)min(max(raw, 0), a.num_blocks - 1) * blk_stride + (size_t)c.kvh * HD * 32;
+    const uint32_t pb = (uint32_t)min(max(raw, 0), a.num_blocks - 1);
+    const uint8_t* g = src + ((uint64_t)pb * blk_stride32 + (uint32_t)(c.kvh * HD * 32));
     const uint32_t l = lds_addr(smem) + stage * STAGE + bw * BLK + j0 * 1024;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) dma_to_lds16<NT>(g + g_off[j], l + j * 1024);
+    dma_to_lds16_run<NT, LPW>(g + g_off, l);
   };
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
@@ -1321,13 +1346,13 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   };
   // Codes of one tile into ring stage `stage` (linear copy of the block); the
   // block's scale is returned (a scalar load, first used a tile later).
+  const uint32_t blk_stride32 = (uint32_t)blk_stride;   // below 2^32 (the planner checks)
   auto issue = [&](const Cursor& c, int raw, int stage) -> float {
-    const size_t pb = (size_t)min(max(raw, 0), a.num_blocks - 1);
-    const uint8_t* g = src + pb * blk_stride + (size_t)c.kvh * BLK8;
+    const uint32_t pb = (uint32_t)min(max(raw, 0), a.num_blocks - 1);
+    const uint8_t* g = src + ((uint64_t)pb * blk_stride32 + (uint32_t)(c.kvh * BLK8));
     const uint32_t l = lds_addr(ring8) + stage * STAGE8 + wave * BLK8;
-#pragma unroll
-    for (int j = 0; j < LPB; ++j) dma_to_lds16<NT>(g + (j * kWave + lane) * 16, l + j * 1024);
-    return scales[pb * a.H_kv + c.kvh];
+    dma_to_lds16_run<NT, LPB>(g + lane * 16, l);
+    return scales[pb * (uint32_t)a.H_kv + (uint32_t)c.kvh];
   };
   // Decoding this wave's block of a tile: the codes of ring stage `stage`
   // (read first, so that the conversion can overlap MFMA work), then their

@@ -102,6 +102,29 @@ def call_attn(p, ws_bytes=1 << 40, **ptrs):
 def test_attn_shape_errors(field, value, status):
     p = good_params()
     setattr(p, field, value)
+    check_attn_status(p, status)
+
+
+@pytest.mark.parametrize("kw", [
+    # one cache block (all KV heads) of 2^31 bytes: 2^20 KV heads x 64 dims x 32 bytes
+    dict(batch=1, draft_len=0, num_q_heads=1 << 20, num_kv_heads=1 << 20, head_dim=64),
+    # 2^32 scale entries
+    dict(num_blocks=1 << 29, num_kv_heads=8),
+])
+def test_attn_size_limits(kw):
+    check_attn_status(good_params(**kw), sv.SV_ERR_UNSUPPORTED)
+    # one step below each limit is accepted by the host checks
+    kw = dict(kw)
+    if "num_blocks" in kw:
+        kw["num_blocks"] -= 1
+    else:
+        kw["num_kv_heads"] = kw["num_q_heads"] = (1 << 20) - 1
+    n = ctypes.c_size_t(0)
+    assert sv.library().spec_verify_attn_workspace_size(ctypes.byref(good_params(**kw)),
+                                                          ctypes.byref(n)) == sv.SV_OK
+
+
+def check_attn_status(p, status):
     n = ctypes.c_size_t(0)
     assert sv.library().spec_verify_attn_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
     assert call_attn(p) == status
