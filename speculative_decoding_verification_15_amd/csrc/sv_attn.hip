@@ -920,7 +920,7 @@ __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* 
 // the offset of sequence b's block-table row are kept alongside, so that the
 // per-tile path does no division or wide multiply.
 struct Cursor {
-  int b, ul, tile, T;
+  int b, tile, T;
   int kvh, mt;
   const int32_t* row;
 };
@@ -938,10 +938,10 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, const int* pref, 
   c.b = lo;
   c.T = uniform((pref[lo + 1] - pref[lo]) / per_seq);
   const int r = g - uniform(pref[lo]);
-  c.ul = r / c.T;
+  const int ul = r / c.T;                   // unit within the sequence: kvh * m_tiles + mt
   c.tile = r % c.T;
-  c.kvh = c.ul / a.m_tiles;
-  c.mt = c.ul % a.m_tiles;
+  c.kvh = ul / a.m_tiles;
+  c.mt = ul % a.m_tiles;
   c.row = a.block_table + (size_t)c.b * a.max_blocks;
   return c;
 }
@@ -957,13 +957,9 @@ __device__ __forceinline__ int unit_tiles(const AttnArgs& a, int b) {
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   if (++c.tile < c.T) return;
   c.tile = 0;
-  ++c.ul;
-  if (++c.mt == a.m_tiles) {
-    c.mt = 0;
-    ++c.kvh;
-  }
-  if (c.ul < a.H_kv * a.m_tiles) return;
-  c.ul = 0;
+  if (++c.mt < a.m_tiles) return;
+  c.mt = 0;
+  if (++c.kvh < a.H_kv) return;
   c.kvh = 0;
   do {
     ++c.b;
@@ -1305,6 +1301,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring8[NS8 * STAGE8];
   __shared__ __attribute__((aligned(1024))) uint8_t img[3 * STAGE];
   __shared__ f32x4 s_mant[3];                 // per image: mantissas of K0, K1, V0, V1 scales
+  __shared__ float s_sink[kLdsThreads];       // put_mant's stores by lanes other than 0
   // the prefix table lives in the images until the first tile is decoded
   static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= 3 * STAGE, "prefix table fits");
   static_assert(NS8 == 3, "the prologue below fills a three-stage code ring");
@@ -1391,7 +1388,10 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   auto put_mant = [&](int im, float scale) {
     float pow2, mant;
     split_scale(scale, pow2, mant);
-    if (lane == 0) reinterpret_cast<float*>(&s_mant[im])[wave] = mant;
+    // lane 0 stores into the slot, the others into sinks of their own: one
+    // store, no branch
+    float* dst = lane == 0 ? reinterpret_cast<float*>(&s_mant[im]) + wave : &s_sink[tid];
+    *dst = mant;
   };
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
@@ -1414,7 +1414,9 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   // Tile t of the range (t = g - g0) is decoded into image t % 3 two tiles
   // ahead of its computation; its scores are computed (MFMA) one tile ahead,
   // under the softmax of the tile before it, as in the bf16 kernel.  sq holds
-  // the scales of the tiles loaded but not yet decoded, oldest first.
+  // the scales of the tiles loaded but not yet decoded, oldest first.  The
+  // code ring has three stages too: i0, i1, i2 = t, t + 1, t + 2 modulo 3
+  // index both, rotated once per tile.
   int gi = g0;
   int ent = entry(ci);
   float sq[NS8];
@@ -1450,8 +1452,8 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   f32x16 xn;                                   // scores of tile g + 1, when have_xn
   bool have_xn = false;
   float m_ref = -INFINITY, l_run = 0.f;
+  int i0 = 0, i1 = 1, i2 = 2;
   for (int g = g0; g < g1; ++g) {
-    const unsigned t = (unsigned)(g - g0);    // unsigned: stage indices are cheap remainders
     // this wave's codes of tile g + 2 landed (tiles g + 3, g + 4 may not have:
     // loads retire in issue order)
     wait_vmcnt<2 * LPB>();
@@ -1480,14 +1482,13 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     }
     // codes of tile g + 2 (decoded in this tile's compute block; past the
     // range the stage holds the last tile again: decoded, never used)
-    const int dstage = (t + 2) % NS8, dimg = (t + 2) % 3;
     u32x4 raw[LPB];
-    dec_read(dstage, raw);
+    dec_read(i2, raw);
     const float dscale = sq[0];
-    put_mant(dimg, dscale);                    // tile g - 1, the image's last user, is done
+    put_mant(i2, dscale);                      // tile g - 1, the image's last user, is done
 
     const int kt = cc.tile * kSkKeys;
-    uint8_t* im = img + (t % 3) * STAGE;
+    uint8_t* im = img + i0 * STAGE;
     if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
       sk_zero_v_tail<HD>(im, kt, r.L);
       __syncthreads();
@@ -1495,13 +1496,13 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     if (active) {
       f32x16 x = have_xn ? xn : sk_scores<HD>(im, k_lds, qop);
       if (kt + kSkKeys - 1 > r.P) sk_mask(x, r, kt);   // unless every key is visible to every row
-      xn = sk_scores<HD>(img + ((t + 1) % 3) * STAGE, k_lds, qop);
-      const f32x4 mt4 = s_mant[t % 3];
+      xn = sk_scores<HD>(img + i1 * STAGE, k_lds, qop);
+      const f32x4 mt4 = s_mant[i0];
       float alpha;
       bf16x8 p[2];
       const bool rescale = softmax_sub_fp8(x, a.c * mt4[0], a.c * mt4[1], mt4[2], mt4[3], m_ref,
                                            l_run, alpha, p[0], p[1]);
-      dec_write(raw, dimg, dscale);
+      dec_write(raw, i2, dscale);
       // probabilities and the decode stay ahead of the rescale branch; the
       // next tile's score MFMAs interleave with the VALU work
       asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
@@ -1522,13 +1523,13 @@ void sv_attn_streamk_fp8(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);       // DS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);       // MFMA
     } else {
-      dec_write(raw, dimg, dscale);
+      dec_write(raw, i2, dscale);
     }
     have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
     // refill the stage just decoded (its codes were consumed above)
     sq[0] = sq[1];
     sq[1] = sq[2];
-    sq[2] = load_next(dstage);
+    sq[2] = load_next(i2);
     if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
       if (active)
         sk_segment_end<HD>(a, r, o, m_ref, l_run,
@@ -1536,6 +1537,10 @@ void sv_attn_streamk_fp8(AttnArgs a) {
                            (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
     if (g + 1 < g1) cursor_next(a, cc);
+    const int i_next = i0;
+    i0 = i1;
+    i1 = i2;
+    i2 = i_next;
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
