@@ -1545,21 +1545,25 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
 
-// Combines the segments of units that straddle range boundaries.  One wave
-// per (unit, 32-row block w, 32-dim block db), laid out like wave w of the
-// stream-K workgroup (lane l holds row 32 w + l % 32 in the accumulator
-// layout), so every partial-O read is 1 KB of consecutive bytes.  A unit's
-// tiles [C, C + T) were split over ranges i = C / Wp .. (C + T - 1) / Wp, and
-// range i holds its segment in slot 0 when the range starts inside the unit,
-// else (the unit began earlier) in slot 1.
+// Combines the segments of units that straddle range boundaries.  One
+// workgroup per (unit, 32-row block w); its wave db takes the 32-dim block db,
+// laid out like wave w of the stream-K workgroup (lane l holds row 32 w + l %
+// 32 in the accumulator layout), so every partial-O read is 1 KB of
+// consecutive bytes.  A unit's tiles [C, C + T) were split over ranges i = C /
+// Wp .. (C + T - 1) / Wp, and range i holds its segment in slot 0 when the
+// range starts inside the unit, else (the unit began earlier) in slot 1.  The
+// segments are merged four at a time with the split-merge rule applied online
+// (running max mu; the sums so far rescaled by 2^(mu_old - mu_new)), so that
+// the (m, l) and O reads of four segments are in flight together.
+constexpr int kMergeBatch = 4;
+
 template <int HD>
-__global__ __launch_bounds__(kWave) void sv_attn_streamk_merge(AttnArgs a) {
-  constexpr int DB = HD / 32;
+__global__ __launch_bounds__(HD / 32 * kWave) void sv_attn_streamk_merge(AttnArgs a) {
   const int waves = a.sk_rows / kRowsPerWave;
-  const int db = blockIdx.x % DB;
-  const int wave = (blockIdx.x / DB) % waves;
-  const int unit = blockIdx.x / (DB * waves);
-  const int lane = threadIdx.x;
+  const int db = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int wave = blockIdx.x % waves;
+  const int unit = blockIdx.x / waves;
   const int per_seq = a.H_kv * a.m_tiles;
   const int b = unit / per_seq;
   const int ul = unit % per_seq;
@@ -1576,20 +1580,36 @@ __global__ __launch_bounds__(kWave) void sv_attn_streamk_merge(AttnArgs a) {
   if (i0 == i1) return;                       // finished in place
   const int row = wave * kRowsPerWave + lane % 32;
   auto slot_of = [&](int i) { return i * 2 + (i * Wp >= C ? 0 : 1); };
-  float mx = -INFINITY;
-  for (int i = i0; i <= i1; ++i)
-    mx = fmaxf(mx, a.ws_ml[(size_t)slot_of(i) * a.sk_rows + row][0]);
-  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float mu = -INFINITY, l = 0.f;
   f32x4 acc[4] = {};
-  float l = 0.f;
-  for (int i = i0; i <= i1; ++i) {
-    const int slot = slot_of(i);
-    const f32x2 ml = a.ws_ml[(size_t)slot * a.sk_rows + row];
-    const float w = fast_exp2(ml[0] - mu);
-    l += w * ml[1];
-    const f32x4* src = sk_partial_o<HD>(a, slot, wave) + lane + db * 4 * kWave;
+  for (int i = i0; i <= i1; i += kMergeBatch) {
+    f32x2 ml[kMergeBatch];
+    f32x4 src[kMergeBatch][4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) acc[q4] += w * src[q4 * kWave];
+    for (int k = 0; k < kMergeBatch; ++k) {   // past i1: segment i1 again, weight 0
+      const int slot = slot_of(min(i + k, i1));
+      ml[k] = a.ws_ml[(size_t)slot * a.sk_rows + row];
+      const f32x4* s = sk_partial_o<HD>(a, slot, wave) + lane + db * 4 * kWave;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) src[k][q4] = s[q4 * kWave];
+    }
+    float mc = mu;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (i + k <= i1) mc = fmaxf(mc, ml[k][0]);
+    const float base = (mc == -INFINITY) ? 0.f : mc;   // exp2(-inf - base) = 0 below
+    const float f = fast_exp2(mu - base);
+    l *= f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) acc[q4] *= f;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float w = (i + k <= i1) ? fast_exp2(ml[k][0] - base) : 0.f;
+      l += w * ml[k][1];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) acc[q4] += w * src[k][q4];
+    }
+    mu = mc;
   }
   const RowCtx r = make_row_ctx(a, 0, kvh, b, clamp_len(a, b), m0, lane);
   if (!r.row_ok) return;
@@ -1840,7 +1860,7 @@ static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = p.B * p.H_kv * p.m_tiles;
-  sv_attn_streamk_merge<HD><<<units * (p.sk_rows / kRowsPerWave) * (HD / 32), kWave, 0, stream>>>(a);
+  sv_attn_streamk_merge<HD><<<units * (p.sk_rows / kRowsPerWave), HD / 32 * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
