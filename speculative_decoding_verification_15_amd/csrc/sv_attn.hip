@@ -1343,12 +1343,18 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   };
   // Codes of one tile into ring stage `stage` (linear copy of the block); the
   // block's scale is returned (a scalar load, first used a tile later).
+  // K codes land in the ring with the slots of each 16-dim group permuted like
+  // the image (bits 2 and 3 of the slot swapped), so that the decode reads and
+  // writes 16-byte vectors in lane order (writes in image order spread eight
+  // consecutive lanes over two 64-byte halves of 128 bytes: a bank conflict).
+  // The permutation stays inside 256 bytes, so one offset serves every 1 KB piece.
   const uint32_t blk_stride32 = (uint32_t)blk_stride;   // below 2^32 (the planner checks)
+  const int g_off8 = moves_v ? lane * 16 : ((lane >> 4) * 16 + swap23(lane & 15)) * 16;
   auto issue = [&](const Cursor& c, int raw, int stage) -> float {
     const uint32_t pb = (uint32_t)min(max(raw, 0), a.num_blocks - 1);
     const uint8_t* g = src + ((uint64_t)pb * blk_stride32 + (uint32_t)(c.kvh * BLK8));
     const uint32_t l = lds_addr(ring8) + stage * STAGE8 + wave * BLK8;
-    dma_to_lds16_run<NT, LPB>(g + lane * 16, l);
+    dma_to_lds16_run<NT, LPB>(g + g_off8, l);
     return scales[pb * (uint32_t)a.H_kv + (uint32_t)c.kvh];
   };
   // Decoding this wave's block of a tile: the codes of ring stage `stage`
@@ -1361,12 +1367,13 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     for (int j = 0; j < LPB; ++j) raw[j] = *reinterpret_cast<const u32x4*>(s8 + (j * kWave + lane) * 16);
   };
   // Image offsets of the two bf16 vectors each code vector becomes (K: 16
-  // dims of key slot p % 16; V: 16 key slots of dim p), fixed per lane.
+  // dims of the key slot image position p % 16 holds; V: 16 key slots of dim
+  // p), fixed per lane.
   int off_lo[LPB], off_hi[LPB];
 #pragma unroll
   for (int j = 0; j < LPB; ++j) {
     const int p = j * kWave + lane;
-    const int k_off = ((2 * (p >> 4)) * 16 + swap23(p & 15)) * 16;
+    const int k_off = ((2 * (p >> 4)) * 16 + (p & 15)) * 16;
     off_lo[j] = wave * BLK + (moves_v ? (2 * p + vhalf_swz(p)) * 16 : k_off);
     off_hi[j] = wave * BLK + (moves_v ? (2 * p + (1 ^ vhalf_swz(p))) * 16 : k_off + 256);
   }
