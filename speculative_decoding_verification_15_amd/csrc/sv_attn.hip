@@ -54,8 +54,10 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* kv_lens;
   uint16_t* out;
-  float* ws_o;    // [B][H_kv][s_max][M][hd] unnormalised O of each split
+  float* ws_o;    // split path: [B][H_kv][s_max][M][hd] unnormalised O of each split;
+                  // stream-K: fp16 O / (l f) of each segment slot (sk_partial_o)
   f32x2* ws_ml;   // [B][H_kv][s_max][M] (m, l) of each split, log2 domain
+  float* ws_f;    // stream-K: power-of-two factor f of each slot row
   int B, R, H_q, H_kv, G, M;
   int max_blocks, num_blocks, max_kv_len;
   int split_tokens, s_max, m_tiles;
@@ -967,13 +969,14 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   c.row = a.block_table + (size_t)c.b * a.max_blocks;
 }
 
-// Partial O of one wave in a segment slot, in the accumulator layout: f32x4
-// number (db * 4 + q4) * 64 + lane holds registers 4 q4 .. 4 q4 + 3 of
-// accumulator block db of that lane (row 32 w + lane % 32, dims
-// 32 db + 8 q4 + 4 (lane / 32) + 0..3).
+// Partial O of one wave in a segment slot: O / (l f) of its rows as fp16, in
+// the accumulator layout: f16x8 number (db * 2 + h) * 64 + lane holds
+// registers 8 h .. 8 h + 7 of accumulator block db of that lane (row 32 w +
+// lane % 32; register 4 q4 + e is dim 32 db + 8 q4 + 4 (lane / 32) + e).  f is
+// the row's power of two (ws_f) that puts its largest |O / l| in [2^14, 2^15).
 template <int HD>
-__device__ __forceinline__ f32x4* sk_partial_o(const AttnArgs& a, int slot, int wave) {
-  return reinterpret_cast<f32x4*>(a.ws_o) + ((size_t)slot * a.sk_rows + wave * kRowsPerWave) * (HD / 4);
+__device__ __forceinline__ f16x8* sk_partial_o(const AttnArgs& a, int slot, int wave) {
+  return reinterpret_cast<f16x8*>(a.ws_o) + ((size_t)slot * a.sk_rows + wave * kRowsPerWave) * (HD / 8);
 }
 
 // Zeroes the V values of keys >= L in the tile image at stage (keys kt ..
@@ -1042,11 +1045,14 @@ __device__ __forceinline__ void sk_pv(const bf16x8 (&vop)[2][HD / 32], const bf1
 }
 
 // Ends a segment of a stream-K range: the unit's output rows when the segment
-// covers the whole unit, else the unnormalised (O, m, l) in segment slot
-// `slot` (the range's first segment or its last one).  O is stored in the
-// accumulator layout (sk_partial_o), every store instruction writing 1 KB of
-// consecutive bytes, and non-temporal: these writes land in the middle of the
-// K/V stream, and ordinary ones cost it several times the bytes they move.
+// covers the whole unit, else (O / l in fp16 with a power-of-two factor per
+// row, m, l) in segment slot `slot` (the range's first segment or its last
+// one).  Two bytes per element instead of fp32 O halve the writes in the
+// middle of the K/V stream (they cost the reads several times their size) and
+// the merge's reads; the per-row factor keeps fp16's 11-bit precision relative
+// to the row's largest value whatever V's range.  Stored in the accumulator
+// layout (sk_partial_o), every store instruction writing 1 KB of consecutive
+// bytes, non-temporal.
 template <int HD>
 __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
                                                const f32x16 (&o)[HD / 32], float m_ref,
@@ -1058,14 +1064,32 @@ __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
     return;
   }
   const float l_tot = halves_sum(l_run);
-  f32x4* dst = sk_partial_o<HD>(a, slot, wave) + lane;
+  float mx = 0.f;                             // largest |O| of the row (both half-waves)
 #pragma unroll
   for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      __builtin_nontemporal_store(
-          f32x4{o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]},
-          dst + (db * 4 + q4) * kWave);
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(o[db][e]));
+  mx = halves_max(mx);
+  // O / l * 2^(15 - ex) with |O| / l < 2^ex: the row's values below 2^15, so
+  // the fp16 result is finite; f = 2^(ex - 15) undoes it.  l = 0 or O = 0
+  // (no visible key, or all-zero V): factor 1 and zeros.
+  const float ol = (l_tot > 0.f) ? mx / l_tot : 0.f;
+  // (ex clamped: with l >= 1 whenever a key is visible, 2^(15 - ex) / l stays finite)
+  const int ex = (ol > 0.f) ? min(max(__builtin_amdgcn_frexp_expf(ol), -100), 127) : 15;
+  const float inv = (l_tot > 0.f) ? __builtin_amdgcn_ldexpf(1.f / l_tot, 15 - ex) : 0.f;
+  f16x8* dst = sk_partial_o<HD>(a, slot, wave) + lane;
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)(o[db][8 * h + e] * inv);
+      __builtin_nontemporal_store(v, dst + (db * 2 + h) * kWave);
+    }
+  if (lane < 32)
+    __builtin_nontemporal_store(__builtin_amdgcn_ldexpf(1.f, ex - 15),
+                                a.ws_f + (size_t)slot * a.sk_rows + wave * kRowsPerWave + lane);
   if (lane < 32)
     __builtin_nontemporal_store(f32x2{m_ref, l_tot},
                                 a.ws_ml + (size_t)slot * a.sk_rows + wave * kRowsPerWave + lane);
@@ -1561,7 +1585,9 @@ void sv_attn_streamk_fp8(AttnArgs a) {
 // range starts inside the unit, else (the unit began earlier) in slot 1.  The
 // segments are merged four at a time with the split-merge rule applied online
 // (running max mu; the sums so far rescaled by 2^(mu_old - mu_new)), so that
-// the (m, l) and O reads of four segments are in flight together.
+// the (m, l) and O reads of four segments are in flight together.  A slot
+// holds O / (l f), so segment s enters the sum of l with weight 2^(m_s - mu)
+// l_s and that of O with the same weight times f_s.
 constexpr int kMergeBatch = 4;
 
 template <int HD>
@@ -1591,14 +1617,16 @@ __global__ __launch_bounds__(HD / 32 * kWave) void sv_attn_streamk_merge(AttnArg
   f32x4 acc[4] = {};
   for (int i = i0; i <= i1; i += kMergeBatch) {
     f32x2 ml[kMergeBatch];
-    f32x4 src[kMergeBatch][4];
+    float fs[kMergeBatch];
+    f16x8 src[kMergeBatch][2];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {   // past i1: segment i1 again, weight 0
       const int slot = slot_of(min(i + k, i1));
       ml[k] = a.ws_ml[(size_t)slot * a.sk_rows + row];
-      const f32x4* s = sk_partial_o<HD>(a, slot, wave) + lane + db * 4 * kWave;
+      fs[k] = a.ws_f[(size_t)slot * a.sk_rows + row];
+      const f16x8* s = sk_partial_o<HD>(a, slot, wave) + lane + db * 2 * kWave;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) src[k][q4] = s[q4 * kWave];
+      for (int h = 0; h < 2; ++h) src[k][h] = s[h * kWave];
     }
     float mc = mu;
 #pragma unroll
@@ -1611,10 +1639,13 @@ __global__ __launch_bounds__(HD / 32 * kWave) void sv_attn_streamk_merge(AttnArg
     for (int q4 = 0; q4 < 4; ++q4) acc[q4] *= f;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const float w = (i + k <= i1) ? fast_exp2(ml[k][0] - base) : 0.f;
-      l += w * ml[k][1];
+      const float w = (i + k <= i1) ? fast_exp2(ml[k][0] - base) * ml[k][1] : 0.f;
+      const float wf = w * fs[k];
+      l += w;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) acc[q4] += w * src[k][q4];
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[q4][e] += wf * (float)src[k][q4 >> 1][4 * (q4 & 1) + e];
     }
     mu = mc;
   }
@@ -1819,9 +1850,10 @@ void plan_attention(AttnPlan& p, int split_request) {
     const size_t slots = (size_t)p.sk_wgs * 2 * p.sk_rows;
     p.ws_meta_offset = 0;
     const size_t meta_bytes = ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256;
-    p.ws_o_bytes = slots * p.hd * sizeof(float);
+    p.ws_o_bytes = slots * p.hd * sizeof(uint16_t);   // fp16 O / (l f)
     p.ws_ml_offset = meta_bytes + p.ws_o_bytes;
-    p.ws_bytes = p.ws_ml_offset + slots * sizeof(f32x2);
+    p.ws_f_offset = p.ws_ml_offset + slots * sizeof(f32x2);
+    p.ws_bytes = p.ws_f_offset + slots * sizeof(float);
     return;
   }
   int split = split_request;
@@ -1923,6 +1955,7 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
     a.ws_o = reinterpret_cast<float*>(ws);
   }
   a.ws_ml = p.ws_bytes ? reinterpret_cast<f32x2*>(ws + p.ws_ml_offset) : nullptr;
+  a.ws_f = p.streamk ? reinterpret_cast<float*>(ws + p.ws_f_offset) : nullptr;
   a.min_tiles = p.min_tiles;
   a.sk_rows = p.sk_rows;
   a.B = p.B;

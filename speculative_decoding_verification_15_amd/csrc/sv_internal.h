@@ -30,6 +30,7 @@ struct AttnPlan {
   int sk_rows;       // rows per stream-K unit: 32 per wave, 4 or 8 waves
   size_t ws_meta_offset;
   size_t ws_o_bytes, ws_ml_offset, ws_bytes;
+  size_t ws_f_offset;  // stream-K: per-slot-row power-of-two factors
 };
 
 struct AttnPtrs {

@@ -180,17 +180,18 @@ def test_attn_workspace_size_formula():
     o_bytes = rows * hd * 4
     assert sv.spec_verify_attn_workspace_size(p) == (o_bytes + 255) // 256 * 256 + rows * 8
     # stream-K path (bf16, 128 rows per KV head): metadata (W, Wp, B + 1 prefix
-    # entries) then two (O, m, l) slots of 128 rows for each of 512 workgroups
+    # entries) then two slots of 128 rows for each of 512 workgroups: O as fp16,
+    # (m, l) as two floats, a power-of-two factor as one float
     p = good_params(max_kv_len=1000)
     slots = 512 * 2 * 128
     meta = ((4 + 3) * 4 + 255) // 256 * 256
-    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
+    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 2 + slots * 8 + slots * 4
     # every shape with B <= 2048 takes that path: fewer than 128 rows per KV
     # head, e4m3 caches
     p = good_params(max_kv_len=1000, draft_len=3, num_q_heads=16)
-    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
+    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 2 + slots * 8 + slots * 4
     p = good_params(max_kv_len=1000, kv_dtype=sv.SV_KV_FP8_E4M3)
-    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 4 + slots * 8
+    assert sv.spec_verify_attn_workspace_size(p) == meta + slots * hd * 2 + slots * 8 + slots * 4
 
 
 @pytest.mark.parametrize("B,D,V,status", [
