@@ -107,3 +107,25 @@ def test_bf16_half_shift_is_caught(monkeypatch):
         return u.view(np.float32).astype(np.float64)
     monkeypatch.setattr(T_fmt, "bf16_bits_to_f64", wrong)
     _expect_pin_failure(T_fmt.test_bf16_all_patterns_match_torch)
+
+
+from tests import test_oracle_accept_sampled as T_smp  # noqa: E402
+
+
+def test_inverted_keep_ratio_is_caught(monkeypatch):
+    # keep with probability min(1, q/p) instead of min(1, p/q)
+    monkeypatch.setattr(acc, "keep_draft", lambda u, p_d, q_d: float(u) * p_d < q_d)
+    _expect_pin_failure(T_smp.test_emitted_tokens_follow_the_target, 1.0)
+
+
+def test_residual_without_subtraction_is_caught(monkeypatch):
+    monkeypatch.setattr(acc, "residual", lambda p_j, q_j: p_j)
+    _expect_pin_failure(T_smp.test_emitted_tokens_follow_the_target, 1.0)
+
+
+def test_draw_off_by_one_is_caught(monkeypatch):
+    def left(w, u):
+        c = np.cumsum(np.asarray(w, np.float64))
+        return min(int(np.searchsorted(c, float(u) * c[-1], side="left")), len(c) - 1)
+    monkeypatch.setattr(T_smp, "oracle_draw", left)
+    _expect_pin_failure(T_smp.test_draw_matches_its_definition, [0.0, 0.2, 0.0, 0.5, 0.3])

@@ -191,3 +191,41 @@ def drafts_from_target(plan: AcceptPlan, target: np.ndarray) -> np.ndarray:
     r = plan.other
     d = np.where(plan.match, t, r + (r >= t))
     return d.astype(np.int32)
+
+
+@dataclasses.dataclass
+class SampledAcceptInputs:
+    w: Workload
+    target_logits: np.ndarray   # [B][R][V] fp32
+    draft_logits: np.ndarray    # [B][D][V] fp32
+    draft: np.ndarray           # [B][D] int32, drawn from softmax(draft_logits / tau)
+    u_accept: np.ndarray        # [B][D] fp32 in [0, 1)
+    u_sample: np.ndarray        # [B] fp32 in [0, 1)
+    tau: float
+
+
+def _uniform01_f32(rng, shape):
+    u = rng.random(shape).astype(np.float32)
+    return np.minimum(u, np.float32(np.nextafter(np.float32(1), np.float32(0))))
+
+
+def make_sampled_accept_inputs(w: Workload, tau: float = 1.0, noise: float = 0.5) -> SampledAcceptInputs:
+    """Inputs of stochastic acceptance: target logits N(0,1); a draft model whose
+    logits are the target's plus N(0, noise^2); drafts drawn from the draft
+    model's distribution at temperature tau by the Gumbel-max trick (the index of
+    the largest y / tau + g with g standard Gumbel, which is a draw from
+    softmax(y / tau) without computing it); uniforms in [0, 1) for the tests and
+    the emitted token.  Streams: SeedSequence([seed, 2]).spawn(5)."""
+    ss = np.random.SeedSequence([w.seed, 2]).spawn(5)
+    rz, ry, rg, ru, rs = (np.random.default_rng(s) for s in ss)
+    z = rz.standard_normal((w.B, w.R, w.V), dtype=np.float32)
+    y = (z[:, : w.D] + np.float32(noise) * ry.standard_normal((w.B, w.D, w.V), dtype=np.float32))
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    draft = np.empty((w.B, w.D), dtype=np.int32)
+    for b in range(w.B):               # per sequence, to bound the temporary
+        g = rg.gumbel(size=(w.D, w.V))
+        draft[b] = np.argmax(y[b].astype(np.float64) / tau + g, axis=-1)
+    return SampledAcceptInputs(w=w, target_logits=z, draft_logits=y, draft=draft,
+                               u_accept=_uniform01_f32(ru, (w.B, w.D)),
+                               u_sample=_uniform01_f32(rs, (w.B,)), tau=float(tau))
+
