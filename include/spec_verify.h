@@ -178,6 +178,53 @@ sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const flo
                       int32_t* out_tokens, const int32_t* kv_lens_in, int32_t* kv_lens_out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace spec_accept_sampled needs for (batch, draft_len, vocab). */
+sv_status spec_accept_sampled_workspace_size(int32_t batch, int32_t draft_len, int32_t vocab,
+                                             size_t* bytes);
+
+/*
+ * Stochastic (lossless) acceptance: the emitted tokens follow the target's own
+ * distribution ("GPU and LLM" ch. 5, section "Speculative decoding (2)"), by the
+ * rule of the paper the pages cite there (Leviathan et al.).
+ *
+ * For sequence b, with p_j = softmax(target_logits[b][j] / temperature) for j in
+ * 0..D and q_j = softmax(draft_logits[b][j] / temperature) for j < D:
+ *     draft j is kept iff  u_accept[b][j] * q_j(d_j) < p_j(d_j)   (d_j = draft[b][j])
+ *     n = first j < D whose draft is not kept, else D
+ *     the emitted token is drawn with u = u_sample[b] from
+ *         max(0, p_n - q_n)   when n < D (p_n itself if that is zero everywhere),
+ *         p_D                 when n = D;
+ *     drawing from weights w: the first v whose running sum of w exceeds u * sum(w)
+ *     accept_len[b]  = n + 1
+ *     out_tokens[b]  = draft[b][0..n) , emitted token , -1 padding
+ *     kv_lens_out[b] = kv_lens_in[b] - (1 + D) + accept_len[b]
+ * The GPU evaluates p and q from fp32 exponentials with fp64 sums; a decision
+ * whose margin lies within that rounding (about 1e-6 relative) may differ from
+ * an exact evaluation.
+ *
+ *   temperature    > 0, finite.
+ *   target_logits  [B][1+D][V] fp32, 16-byte aligned.  Finite or -inf, at least
+ *                  one finite value per row.
+ *   draft_logits   [B][D][V] fp32, 16-byte aligned: the draft model's logits the
+ *                  drafts were drawn from (same conditions; NULL when D = 0).
+ *   draft          [B][D] int32 (NULL when D = 0); ids are clamped into [0, V)
+ *                  for the keep test and copied unchanged into out_tokens.
+ *   u_accept       [B][D] fp32 uniforms in [0, 1) (NULL when D = 0).
+ *   u_sample       [B] fp32 uniforms in [0, 1).
+ *   accept_len, out_tokens, kv_lens_in, kv_lens_out as for spec_accept
+ *                  (kv_lens_out may alias kv_lens_in).
+ *   workspace      at least spec_accept_sampled_workspace_size() bytes,
+ *                  256-byte aligned.
+ * Errors: SV_ERR_INVALID for shapes, temperature, NULL or misaligned pointers;
+ * SV_ERR_UNSUPPORTED when batch * (1 + 2 draft_len) > 65535; SV_ERR_WORKSPACE.
+ */
+sv_status spec_accept_sampled(int32_t batch, int32_t draft_len, int32_t vocab, float temperature,
+                              const float* target_logits, const float* draft_logits,
+                              const int32_t* draft, const float* u_accept, const float* u_sample,
+                              int32_t* accept_len, int32_t* out_tokens, const int32_t* kv_lens_in,
+                              int32_t* kv_lens_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Static description of a status code. */
 const char* sv_status_string(sv_status s);
 

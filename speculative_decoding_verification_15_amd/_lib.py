@@ -19,7 +19,8 @@ SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1
 
 # Every symbol include/spec_verify.h declares.
 EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_workspace_size",
-           "spec_accept", "sv_status_string", "sv_last_error", "sv_abi_version")
+           "spec_accept", "spec_accept_sampled_workspace_size", "spec_accept_sampled",
+           "sv_status_string", "sv_last_error", "sv_abi_version")
 
 
 class SvAttnParams(ctypes.Structure):
@@ -63,6 +64,10 @@ def _load():
     lib.spec_accept_workspace_size.restype = U
     lib.spec_accept.argtypes = [I32, I32, I32] + [P] * 8 + [S, P]
     lib.spec_accept.restype = U
+    lib.spec_accept_sampled_workspace_size.argtypes = [I32, I32, I32, ctypes.POINTER(S)]
+    lib.spec_accept_sampled_workspace_size.restype = U
+    lib.spec_accept_sampled.argtypes = [I32, I32, I32, ctypes.c_float] + [P] * 10 + [S, P]
+    lib.spec_accept_sampled.restype = U
     lib.sv_status_string.argtypes = [U]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -153,3 +158,23 @@ def spec_accept(batch, draft_len, vocab, logits, draft, target_tokens, accept_le
     _check(_lib.spec_accept(batch, draft_len, vocab, _ptr(logits), _ptr(draft), _ptr(target_tokens),
                             _ptr(accept_len), _ptr(out_tokens), _ptr(kv_lens_in), _ptr(kv_lens_out),
                             _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def spec_accept_sampled_workspace_size(batch: int, draft_len: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.spec_accept_sampled_workspace_size(batch, draft_len, vocab, ctypes.byref(n)))
+    return int(n.value)
+
+
+def spec_accept_sampled(batch, draft_len, vocab, temperature, target_logits, draft_logits, draft,
+                        u_accept, u_sample, accept_len, out_tokens, kv_lens_in, kv_lens_out,
+                        workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(_lib.spec_accept_sampled(batch, draft_len, vocab, float(temperature),
+                                    _ptr(target_logits), _ptr(draft_logits), _ptr(draft),
+                                    _ptr(u_accept), _ptr(u_sample), _ptr(accept_len),
+                                    _ptr(out_tokens), _ptr(kv_lens_in), _ptr(kv_lens_out),
+                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+

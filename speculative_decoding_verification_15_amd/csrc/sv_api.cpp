@@ -181,6 +181,60 @@ sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const flo
   return SV_OK;
 }
 
+static sv_status check_sampled_shape(int32_t batch, int32_t draft_len, int32_t vocab,
+                                     float temperature) {
+  sv_status s = check_accept_shape(batch, draft_len, vocab);
+  if (s != SV_OK) return s;
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SV_ERR_INVALID, "temperature must be finite and > 0");
+  const long long rows = (long long)batch * (2 * draft_len + 1);
+  if (rows > kMaxGridYZ)
+    return fail(SV_ERR_UNSUPPORTED, "batch * (1 + 2 draft_len) > %d", kMaxGridYZ);
+  return SV_OK;
+}
+
+sv_status spec_accept_sampled_workspace_size(int32_t batch, int32_t draft_len, int32_t vocab,
+                                             size_t* bytes) {
+  if (!bytes) return fail(SV_ERR_INVALID, "bytes is NULL");
+  sv_status s = check_sampled_shape(batch, draft_len, vocab, 1.f);
+  if (s != SV_OK) return s;
+  *bytes = sv::accept_sampled_workspace_bytes(batch, draft_len, vocab);
+  return SV_OK;
+}
+
+sv_status spec_accept_sampled(int32_t batch, int32_t draft_len, int32_t vocab, float temperature,
+                              const float* target_logits, const float* draft_logits,
+                              const int32_t* draft, const float* u_accept, const float* u_sample,
+                              int32_t* accept_len, int32_t* out_tokens, const int32_t* kv_lens_in,
+                              int32_t* kv_lens_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  sv_status s = check_sampled_shape(batch, draft_len, vocab, temperature);
+  if (s != SV_OK) return s;
+  if (!target_logits || !u_sample || !accept_len || !out_tokens || !kv_lens_in || !kv_lens_out)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (draft_len > 0 && (!draft_logits || !draft || !u_accept))
+    return fail(SV_ERR_INVALID, "draft_logits, draft and u_accept are required with draft_len > 0");
+  if (!aligned(target_logits, 16) || (draft_logits && !aligned(draft_logits, 16)))
+    return fail(SV_ERR_INVALID, "logits must be 16-byte aligned");
+  if (!aligned(u_sample, 4) || (u_accept && !aligned(u_accept, 4)))
+    return fail(SV_ERR_INVALID, "uniform arrays must be 4-byte aligned");
+  if (!aligned(accept_len, 4) || !aligned(out_tokens, 4) || !aligned(kv_lens_in, 4) ||
+      !aligned(kv_lens_out, 4) || (draft && !aligned(draft, 4)))
+    return fail(SV_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  const size_t need = sv::accept_sampled_workspace_bytes(batch, draft_len, vocab);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(SV_ERR_INVALID, "workspace must be 256-byte aligned");
+  hipError_t e = sv::launch_accept_sampled(batch, draft_len, vocab, temperature, target_logits,
+                                           draft_logits, draft, u_accept, u_sample, accept_len,
+                                           out_tokens, kv_lens_in, kv_lens_out, workspace,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
 const char* sv_status_string(sv_status s) {
   switch (s) {
     case SV_OK: return "SV_OK";

@@ -61,4 +61,16 @@ hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t
                          int32_t* target, int32_t* accept_len, int32_t* out_tokens,
                          const int32_t* kv_in, int32_t* kv_out, void* ws, hipStream_t stream);
 
+// Stochastic acceptance: one (max, fp64 sum) record of 16 bytes per 4096-logit
+// chunk of every target row (B (1 + D)) and draft row (B D).
+inline size_t accept_sampled_workspace_bytes(int B, int D, int V) {
+  return (size_t)B * (size_t)(2 * D + 1) * (size_t)argmax_chunks(V) * 16u;
+}
+
+hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt, const float* zd,
+                                 const int32_t* draft, const float* u_accept,
+                                 const float* u_sample, int32_t* accept_len, int32_t* out_tokens,
+                                 const int32_t* kv_in, int32_t* kv_out, void* ws,
+                                 hipStream_t stream);
+
 }  // namespace sv

@@ -248,3 +248,53 @@ def test_every_kernel_launch_stub_is_defined():
     out = subprocess.run(["nm", "-D", "--undefined-only", sv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert "__device_stub__" not in out
+
+
+def call_sampled(B=4, D=3, V=1000, tau=1.0, ws_bytes=1 << 40, **ptrs):
+    a = dict(zt=FAKE, zd=FAKE, draft=FAKE, ua=FAKE, us=FAKE, al=FAKE, out=FAKE, kvi=FAKE,
+             kvo=FAKE, ws=FAKE * 4)
+    a.update(ptrs)
+    return sv.library().spec_accept_sampled(B, D, V, tau, a["zt"], a["zd"], a["draft"], a["ua"],
+                                            a["us"], a["al"], a["out"], a["kvi"], a["kvo"],
+                                            a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("B,D,V,tau,status", [
+    (0, 3, 100, 1.0, sv.SV_ERR_INVALID), (2, -1, 100, 1.0, sv.SV_ERR_INVALID),
+    (2, 64, 100, 1.0, sv.SV_ERR_INVALID), (2, 3, 0, 1.0, sv.SV_ERR_INVALID),
+    (2, 3, 100, 0.0, sv.SV_ERR_INVALID), (2, 3, 100, -1.0, sv.SV_ERR_INVALID),
+    (2, 3, 100, float("inf"), sv.SV_ERR_INVALID), (2, 3, 100, float("nan"), sv.SV_ERR_INVALID),
+    (10000, 3, 100, 1.0, sv.SV_ERR_UNSUPPORTED),      # 10000 * 7 rows > 65535
+])
+def test_sampled_shape_errors(B, D, V, tau, status):
+    assert call_sampled(B, D, V, tau) == status
+    if tau == 1.0:
+        n = ctypes.c_size_t(0)
+        assert sv.library().spec_accept_sampled_workspace_size(B, D, V, ctypes.byref(n)) == status
+
+
+@pytest.mark.parametrize("ptrs,status", [
+    (dict(zt=None), sv.SV_ERR_INVALID), (dict(us=None), sv.SV_ERR_INVALID),
+    (dict(al=None), sv.SV_ERR_INVALID), (dict(out=None), sv.SV_ERR_INVALID),
+    (dict(kvi=None), sv.SV_ERR_INVALID), (dict(kvo=None), sv.SV_ERR_INVALID),
+    (dict(zd=None), sv.SV_ERR_INVALID), (dict(draft=None), sv.SV_ERR_INVALID),
+    (dict(ua=None), sv.SV_ERR_INVALID),
+    (dict(zt=FAKE + 4), sv.SV_ERR_INVALID), (dict(zd=FAKE + 8), sv.SV_ERR_INVALID),
+    (dict(us=FAKE + 2), sv.SV_ERR_INVALID), (dict(draft=FAKE + 2), sv.SV_ERR_INVALID),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE), (dict(ws=FAKE + 64), sv.SV_ERR_INVALID),
+])
+def test_sampled_pointer_errors(ptrs, status):
+    assert call_sampled(**ptrs) == status
+
+
+def test_sampled_no_drafts_allows_null_draft_arrays():
+    # D = 0: draft_logits, draft and u_accept may be NULL (checked up to the workspace error)
+    assert call_sampled(D=0, zd=None, draft=None, ua=None, ws=None) == sv.SV_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("B,D,V", [(1, 0, 1), (4, 3, 1024), (32, 15, 128256), (3, 63, 8193)])
+def test_sampled_workspace_size(B, D, V):
+    chunks = -(-V // 4096)
+    need = B * (2 * D + 1) * chunks * 16          # (max, fp64 sum) per chunk of every row
+    assert sv.spec_accept_sampled_workspace_size(B, D, V) == need
+    assert call_sampled(B, D, V, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
