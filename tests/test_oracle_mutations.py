@@ -129,3 +129,47 @@ def test_draw_off_by_one_is_caught(monkeypatch):
         return min(int(np.searchsorted(c, float(u) * c[-1], side="left")), len(c) - 1)
     monkeypatch.setattr(T_smp, "oracle_draw", left)
     _expect_pin_failure(T_smp.test_draw_matches_its_definition, [0.0, 0.2, 0.0, 0.5, 0.3])
+
+
+import oracle.append as app  # noqa: E402
+from tests import test_oracle_append as T_app  # noqa: E402
+
+
+def test_block_scale_without_448_is_caught(monkeypatch):
+    # scale = amax (codes would top out at 1.0 instead of 448)
+    monkeypatch.setattr(app, "_block_scale", lambda amax: np.float32(amax) if amax else np.float32(1))
+    _expect_pin_failure(T_app.test_block_aligned_appends_match_generator_placement, True)
+
+
+def test_encode_ties_away_from_zero_is_caught(monkeypatch):
+    real = app.e4m3_encode_f32
+
+    def away(y):
+        y = np.asarray(y, np.float32)
+        # nudge exact halfway cases upwards before the correct encoder
+        return real(np.nextafter(y, np.sign(y) * np.float32(np.inf)).astype(np.float32))
+    monkeypatch.setattr(app, "e4m3_encode_f32", away)
+    _expect_pin_failure(T_app.test_block_aligned_appends_match_generator_placement, True)
+
+
+def test_held_codes_not_reencoded_is_caught(monkeypatch):
+    # on a scale change the held codes keep their old bytes (their values change)
+    real = app.oracle_kv_append
+
+    def no_reencode(k_new, v_new, k_cache, v_cache, k_scale, v_scale, table, lens, fp8):
+        out = real(k_new, v_new, k_cache, v_cache, k_scale, v_scale, table, lens, fp8)
+        kc = out[0]
+        for b, c in enumerate(np.asarray(lens)):
+            blk, a = table[b][int(c) // 16], int(c) % 16
+            kc[blk, :, :, :a, :] = np.asarray(k_cache)[blk, :, :, :a, :]
+        return out
+    monkeypatch.setattr(T_app, "oracle_kv_append", no_reencode)
+    _expect_pin_failure(T_app.test_fp8_held_codes_kept_when_values_fit_and_reencoded_when_they_outgrow)
+
+
+def test_append_at_wrong_position_is_caught(monkeypatch):
+    real = app.oracle_kv_append
+    monkeypatch.setattr(T_app, "oracle_kv_append",
+                        lambda kn, vn, kc, vc, ks, vs, t, lens, fp8:
+                        real(kn, vn, kc, vc, ks, vs, t, np.asarray(lens) + 1, fp8))
+    _expect_pin_failure(T_app.test_bf16_rows_land_where_the_attention_gather_reads_them)

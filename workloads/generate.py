@@ -229,3 +229,29 @@ def make_sampled_accept_inputs(w: Workload, tau: float = 1.0, noise: float = 0.5
                                u_accept=_uniform01_f32(ru, (w.B, w.D)),
                                u_sample=_uniform01_f32(rs, (w.B,)), tau=float(tau))
 
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    """A paged cache holding each sequence's committed tokens, and the K/V rows of
+    its R new positions to append."""
+    base: AttnInputs            # cache, scales and block table (room for c_b + R tokens)
+    committed: np.ndarray       # [B] int32: c_b, tokens held before the append
+    k_new: np.ndarray           # [B][R][H_kv][hd] bf16 bits
+    v_new: np.ndarray
+
+
+def make_append_inputs(w: Workload, gains=(1.0,)) -> AppendInputs:
+    """The cache of ``make_attn_inputs(w)`` with its committed length set to the
+    context T_b (the R positions after it are overwritten by the append), and new
+    K/V rows N(0,1) * g, g drawn per (sequence, KV head) from ``gains`` (gains
+    above 1 make appended values outgrow a block's e4m3 scale).
+    Streams: SeedSequence([seed, 3]).spawn(3) in the order k, v, gain."""
+    base = make_attn_inputs(w)
+    ss = np.random.SeedSequence([w.seed, 3]).spawn(3)
+    rk, rv, rg = (np.random.default_rng(s) for s in ss)
+    g = np.asarray(gains, dtype=np.float32)[rg.integers(0, len(gains), size=(w.B, 1, w.H_kv, 1))]
+    k = rk.standard_normal((w.B, w.R, w.H_kv, w.hd), dtype=np.float32) * g
+    v = rv.standard_normal((w.B, w.R, w.H_kv, w.hd), dtype=np.float32) * g
+    return AppendInputs(base=base, committed=(base.kv_lens - w.R).astype(np.int32),
+                        k_new=f32_to_bf16_bits(k), v_new=f32_to_bf16_bits(v))
