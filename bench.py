@@ -36,7 +36,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "verified tokens/sec + KV HBM GB/s (% peak) at Llama-70B-like GQA, D=15"
 KERNEL_SOURCES = ("speculative_decoding_verification_15_amd/csrc/sv_attn.hip",
                   "speculative_decoding_verification_15_amd/csrc/sv_device.h",
-                  "speculative_decoding_verification_15_amd/csrc/sv_internal.h")
+                  "speculative_decoding_verification_15_amd/csrc/sv_attn_plan.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sv_attn.md")
 
 
@@ -94,6 +94,75 @@ def read_traffic(src_hash):
     if not m or m.group(1) != src_hash:
         return None
     return {"workload": m.group(2), "bytes": int(m.group(3))}
+
+
+def time_append(w, da, stream, sv, calls=20):
+    """spec_kv_append of the step's R new rows per sequence at the committed length
+    T_b (the slots the attention reads last), timed with HIP events after the
+    step's own timing.  Not part of the step: the cache of the workload already
+    holds those rows."""
+    import torch
+    from tests.gpu_util import dev
+    from workloads import make_append_inputs
+    ap = make_append_inputs(w, base=da.inp)
+    kn, vn = dev(ap.k_new), dev(ap.v_new)
+    kin = dev(ap.committed)
+    kout = torch.empty_like(kin)
+    fp8 = w.kv_dtype == "fp8_e4m3"
+    prm = sv.make_append_params(batch=w.B, num_new=w.R, num_kv_heads=w.H_kv, head_dim=w.hd,
+                                max_blocks_per_seq=da.inp.block_table.shape[1],
+                                num_blocks=da.inp.num_blocks,
+                                kv_dtype=sv.SV_KV_FP8_E4M3 if fp8 else sv.SV_KV_BF16)
+    sh = stream.cuda_stream
+    sv.spec_kv_append(prm, kn, vn, da.k, da.v, da.ks, da.vs, da.bt, kin, kout, stream=sh)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(calls):
+        sv.spec_kv_append(prm, kn, vn, da.k, da.v, da.ks, da.vs, da.bt, kin, kout, stream=sh)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / calls
+    rows = w.B * w.R * w.H_kv * 2
+    moved = rows * w.hd * (2 + (1 if fp8 else 2))     # bf16 rows in, cache rows out
+    return {"kernel": "sv_kv_append", "avg_launch_us": round(us, 2),
+            "bytes_new_rows_in_and_out": moved, "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+
+
+def time_accept_sampled(w, da, stream, sv, calls=20):
+    """spec_accept_sampled (lossless stochastic acceptance) on the workload's shape:
+    target logits [B][1+D][V], draft logits [B][D][V], timed with HIP events after
+    the step's own timing.  The greedy spec_accept is the step's acceptance; this
+    is its sampled-decoding counterpart."""
+    import torch
+    from tests.gpu_util import dev
+    from workloads import make_sampled_accept_inputs
+    si = make_sampled_accept_inputs(w)
+    B, D, V = w.B, w.D, w.V
+    zt, zd = dev(si.target_logits), dev(si.draft_logits)
+    dr, ua, us = dev(si.draft), dev(si.u_accept), dev(si.u_sample)
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, w.R), dtype=torch.int32, device="cuda")
+    kout = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ws_bytes = sv.spec_accept_sampled_workspace_size(B, D, V)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sh = stream.cuda_stream
+
+    def call():
+        sv.spec_accept_sampled(B, D, V, si.tau, zt, zd, dr, ua, us, al, out, da.kl, kout, ws,
+                               ws_bytes, stream=sh)
+    call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(calls):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us_call = ev[0].elapsed_time(ev[1]) * 1e3 / calls
+    # every target and draft logit once, plus the one row each sequence draws from
+    moved = (B * (2 * D + 1) * V + B * V) * 4
+    return {"kernels": "sv_sample_stats + sv_sample_decide", "avg_launch_us": round(us_call, 2),
+            "algorithmic_bytes": moved, "GBps": round(moved / (us_call * 1e-6) / 1e9, 1),
+            "sum_accept_len": int(al.cpu().sum())}
 
 
 def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
@@ -224,6 +293,9 @@ def main():
         al_per_set.append(int(al.cpu().sum()))
     tokens_timed = sum(al_per_set[i % n_sets] for i in range(args.steps))
 
+    append = time_append(w, da, stream, sv)
+    sampled = time_accept_sampled(w, da, stream, sv)
+
     ms_per_step = total_ms / args.steps
     value = tokens_timed / (total_ms / 1e3)
     attn_us = float(np.mean(t_attn) * 1e3)
@@ -271,6 +343,8 @@ def main():
                  "algorithmic_flops_per_launch": flops},
         "accept": {"avg_launch_us": round(acc_us, 2),
                    "GBps": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9, 1)},
+        "append": append,
+        "accept_sampled": sampled,
         "sum_accept_len_per_step": round(tokens_timed / args.steps, 2),
         "kernel_src_sha": src_hash,
         "input_gen_s": round(t_gen, 1),

@@ -4,8 +4,11 @@
  *
  * The verification step scores the D drafted tokens of each sequence plus one
  * bonus position in a single target pass, then keeps the drafts up to the first
- * one the target disagrees with.  Two calls cover it:
+ * one the target disagrees with.  The calls:
  *
+ *   spec_kv_append     writes the K/V rows of the new positions into the paged
+ *                      cache (e4m3 caches: quantize on write) and grows the
+ *                      lengths; the step before attention.
  *   spec_verify_attn   attention of the R = D + 1 new positions of every
  *                      sequence over its paged KV cache (GQA: G = H_q / H_kv
  *                      query heads share one KV head, so G * R query rows read
@@ -14,6 +17,8 @@
  *   spec_accept        per-row argmax of the target logits, first-mismatch
  *                      prefix against the drafts, acceptance length and the
  *                      committed KV length.
+ *   spec_accept_sampled  the same for sampled decoding: lossless stochastic
+ *                      acceptance of the drafts and a draw of the next token.
  *
  * Where the operations are defined (the pages this library implements):
  *   - one target pass over the drafted positions plus the bonus position, and
@@ -224,6 +229,66 @@ sv_status spec_accept_sampled(int32_t batch, int32_t draft_len, int32_t vocab, f
                               int32_t* accept_len, int32_t* out_tokens, const int32_t* kv_lens_in,
                               int32_t* kv_lens_out, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Shape of one spec_kv_append call.  Sizes are element counts. */
+typedef struct sv_append_params {
+  int32_t batch;              /* B >= 1 sequences */
+  int32_t num_new;            /* R >= 1 rows appended per sequence (1 + D at a
+                                 verification step), <= 16 * max_blocks_per_seq */
+  int32_t num_kv_heads;       /* H_kv >= 1 */
+  int32_t head_dim;           /* hd: 64 or 128 */
+  int32_t block_size;         /* tokens per KV block: must be 16 */
+  int32_t max_blocks_per_seq; /* columns of block_table, 16 * max_blocks_per_seq < 2^31 */
+  int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
+  int32_t kv_dtype;           /* an sv_kv_dtype */
+} sv_append_params;
+
+/*
+ * KV append: the step before spec_verify_attn.  The K and V rows of the R new
+ * positions of every sequence are written into its paged cache at token
+ * positions c_b .. c_b + R - 1, c_b = kv_lens_in[b] (the committed length), and
+ * kv_lens_out[b] = c_b + R, the L_b spec_verify_attn takes.  Rejected drafts need
+ * no undo here: spec_accept lowers the length, and the next append writes over
+ * the slots past it.  Paged blocks: "GPU and LLM" ch. 5, section "PagedAttention
+ * (2)"; FP8 KV with scaling factors, updated as the cache grows: novita.ai blog,
+ * sections "Proprietary FP8 quantization scheme" and "KVCache quantization".
+ *
+ * bf16 caches: the rows are stored as given.
+ * e4m3 caches, per (physical block, KV head), for K and V separately, with
+ * a = slots of the block held before the call and amax_new = the largest
+ * |value| appended to the block:
+ *   - a = 0 (the block starts here): scale = amax_new / 448 (1 if amax_new = 0);
+ *   - a > 0, amax_new <= fp32(max_held |decode(code)| * scale): scale and held
+ *     codes stay;
+ *   - otherwise scale = amax_new / 448 and every held code is re-encoded from
+ *     fp32(decode(code) * old scale).
+ *   A value x is stored as e4m3(fp32(x / scale)): the nearest e4m3 value, ties to
+ *   the even code, magnitudes of 448 and above saturated to 448, sign bit of the
+ *   quotient.  Slots other than those written, and the scales of blocks not
+ *   written, keep their bytes.
+ *
+ *   k_new, v_new   [B][R][H_kv][hd] bf16, finite.                  16-byte aligned.
+ *   k_cache, v_cache, k_scale, v_scale, block_table: layouts as for
+ *                  spec_verify_attn (scales required for e4m3, NULL for bf16);
+ *                  caches 16-byte aligned.  Read and written.
+ *   kv_lens_in     [B] int32, c_b.
+ *   kv_lens_out    [B] int32, written c_b + R; may be the same pointer as
+ *                  kv_lens_in.
+ *
+ * Device preconditions: 0 <= c_b <= 16 * max_blocks_per_seq - R;
+ * block_table[b][j] in [0, num_blocks) for the blocks j = c_b / 16 ..
+ * (c_b + R - 1) / 16, and no physical block written by this call appears in
+ * two of those places; the held slots of a block whose scale is in use hold
+ * finite codes.  A length outside its range is clamped (giving kv_lens_out =
+ * clamped length + R) and table entries are clamped into [0, num_blocks), so
+ * no access leaves the buffers.
+ * Errors: SV_ERR_INVALID for shapes, NULL or misaligned pointers, scales given
+ * for bf16 or missing for e4m3; SV_ERR_UNSUPPORTED for head_dim or block_size.
+ */
+sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* block_table, const int32_t* kv_lens_in,
+                         int32_t* kv_lens_out, void* stream);
 
 /* Static description of a status code. */
 const char* sv_status_string(sv_status s);

@@ -20,7 +20,7 @@ SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1
 # Every symbol include/spec_verify.h declares.
 EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_workspace_size",
            "spec_accept", "spec_accept_sampled_workspace_size", "spec_accept_sampled",
-           "sv_status_string", "sv_last_error", "sv_abi_version")
+           "spec_kv_append", "sv_status_string", "sv_last_error", "sv_abi_version")
 
 
 class SvAttnParams(ctypes.Structure):
@@ -37,6 +37,19 @@ class SvAttnParams(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("split_tokens", ctypes.c_int32),
+    ]
+
+
+class SvAppendParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_new", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -68,6 +81,8 @@ def _load():
     lib.spec_accept_sampled_workspace_size.restype = U
     lib.spec_accept_sampled.argtypes = [I32, I32, I32, ctypes.c_float] + [P] * 10 + [S, P]
     lib.spec_accept_sampled.restype = U
+    lib.spec_kv_append.argtypes = [ctypes.POINTER(SvAppendParams)] + [P] * 10
+    lib.spec_kv_append.restype = U
     lib.sv_status_string.argtypes = [U]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -178,3 +193,16 @@ def spec_accept_sampled(batch, draft_len, vocab, temperature, target_logits, dra
                                     _ptr(out_tokens), _ptr(kv_lens_in), _ptr(kv_lens_out),
                                     _ptr(workspace), workspace_bytes, _stream(stream)))
 
+
+
+def make_append_params(*, batch, num_new, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
+                       kv_dtype=SV_KV_BF16, block_size=16) -> SvAppendParams:
+    return SvAppendParams(batch, num_new, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                          num_blocks, kv_dtype)
+
+
+def spec_kv_append(params: SvAppendParams, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                   block_table, kv_lens_in, kv_lens_out, stream=None) -> None:
+    _check(_lib.spec_kv_append(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                               _ptr(kv_lens_in), _ptr(kv_lens_out), _stream(stream)))

@@ -235,6 +235,51 @@ sv_status spec_accept_sampled(int32_t batch, int32_t draft_len, int32_t vocab, f
   return SV_OK;
 }
 
+sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* block_table, const int32_t* kv_lens_in,
+                         int32_t* kv_lens_out, void* stream) {
+  if (!p) return fail(SV_ERR_INVALID, "params is NULL");
+  if (p->batch < 1) return fail(SV_ERR_INVALID, "batch must be >= 1 (got %d)", p->batch);
+  if (p->num_new < 1) return fail(SV_ERR_INVALID, "num_new must be >= 1 (got %d)", p->num_new);
+  if (p->num_kv_heads < 1) return fail(SV_ERR_INVALID, "num_kv_heads must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->block_size != 16)
+    return fail(SV_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", p->block_size);
+  if (p->kv_dtype != SV_KV_BF16 && p->kv_dtype != SV_KV_FP8_E4M3)
+    return fail(SV_ERR_INVALID, "unknown kv_dtype %d", p->kv_dtype);
+  if (p->num_blocks < 1) return fail(SV_ERR_INVALID, "num_blocks must be >= 1");
+  if (p->max_blocks_per_seq < 1 || (long long)p->max_blocks_per_seq * 16 >= (1LL << 31))
+    return fail(SV_ERR_INVALID, "max_blocks_per_seq must be in [1, 2^27) (got %d)",
+                p->max_blocks_per_seq);
+  if ((long long)p->num_new > (long long)p->max_blocks_per_seq * 16)
+    return fail(SV_ERR_INVALID, "num_new (%d) exceeds the table's %lld tokens", p->num_new,
+                (long long)p->max_blocks_per_seq * 16);
+  const bool fp8 = p->kv_dtype == SV_KV_FP8_E4M3;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !kv_lens_in || !kv_lens_out)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(SV_ERR_INVALID, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(kv_lens_in, 4) || !aligned(kv_lens_out, 4))
+    return fail(SV_ERR_INVALID, "block_table and kv_lens must be 4-byte aligned");
+  if (fp8) {
+    if (!k_scale || !v_scale) return fail(SV_ERR_INVALID, "e4m3 caches need k_scale and v_scale");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4))
+      return fail(SV_ERR_INVALID, "k_scale and v_scale must be 4-byte aligned");
+  } else if (k_scale || v_scale) {
+    return fail(SV_ERR_INVALID, "k_scale and v_scale must be NULL for bf16 caches");
+  }
+  sv::AppendPlan plan{p->batch, p->num_new, p->num_kv_heads, p->head_dim, p->max_blocks_per_seq,
+                      p->num_blocks, fp8};
+  hipError_t e = sv::launch_kv_append(plan, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                      block_table, kv_lens_in, kv_lens_out,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
 const char* sv_status_string(sv_status s) {
   switch (s) {
     case SV_OK: return "SV_OK";

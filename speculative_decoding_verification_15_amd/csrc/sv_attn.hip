@@ -41,7 +41,7 @@
 // reach a row.  All softmax arithmetic runs in the log2 domain
 // (x = s * sm_scale * log2 e, exp2).
 #include "sv_device.h"
-#include "sv_internal.h"
+#include "sv_attn_plan.h"
 
 namespace sv {
 

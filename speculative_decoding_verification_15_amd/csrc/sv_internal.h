@@ -1,5 +1,6 @@
 // Host-side interface between the C ABI layer (sv_api.cpp) and the kernel
-// launchers (sv_attn.hip, sv_accept.hip).  Arguments reaching these launchers
+// launchers (attention: sv_attn_plan.h; acceptance, sampled acceptance and KV
+// append below).  Arguments reaching these launchers
 // have already been validated.
 #pragma once
 
@@ -7,47 +8,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sv_attn_plan.h"
+
 namespace sv {
-
-// Keys per attention tile iteration; split boundaries are multiples of it.
-constexpr int kAttnTile = 64;
-// Query rows per wave (one 32-wide MFMA operand).
-constexpr int kRowsPerWave = 32;
-
-struct AttnPlan {
-  int B, R, H_q, H_kv, G, M, hd;
-  int max_blocks, num_blocks, max_kv_len;
-  bool fp8;
-  float sm_scale;
-  int split_tokens;  // keys per split (multiple of kAttnTile)
-  int s_max;         // ceil(max_kv_len / split_tokens)
-  int waves;         // waves per workgroup (each owns 32 query rows)
-  int m_tiles;       // ceil(M / (32 * waves))
-  // stream-K path (bf16 cache, 128-row tiles): persistent workgroups, the least
-  // number of 64-key tiles per workgroup, and the metadata block in the workspace
-  bool streamk;
-  int sk_wgs, min_tiles;
-  int sk_rows;       // rows per stream-K unit: 32 per wave, 4 or 8 waves
-  size_t ws_meta_offset;
-  size_t ws_o_bytes, ws_ml_offset, ws_bytes;
-  size_t ws_f_offset;  // stream-K: per-slot-row power-of-two factors
-};
-
-struct AttnPtrs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* k_scale;
-  const float* v_scale;
-  const int32_t* block_table;
-  const int32_t* kv_lens;
-  void* out;
-  void* ws;
-};
-
-// Fills split/grid/workspace fields of `plan` from its shape fields.
-void plan_attention(AttnPlan& plan, int split_tokens_request);
-hipError_t launch_attention(const AttnPlan& plan, const AttnPtrs& ptrs, hipStream_t stream);
 
 constexpr int kArgmaxThreads = 256;
 constexpr int kArgmaxChunk = kArgmaxThreads * 4 * 4;  // logits per workgroup
@@ -72,5 +35,16 @@ hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt
                                  const float* u_sample, int32_t* accept_len, int32_t* out_tokens,
                                  const int32_t* kv_in, int32_t* kv_out, void* ws,
                                  hipStream_t stream);
+
+// KV append (sv_append.hip): one workgroup per sequence.
+struct AppendPlan {
+  int B, R, H_kv, hd, max_blocks, num_blocks;
+  bool fp8;
+};
+
+hipError_t launch_kv_append(const AppendPlan& plan, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                            const int32_t* table, const int32_t* kv_in, int32_t* kv_out,
+                            hipStream_t stream);
 
 }  // namespace sv

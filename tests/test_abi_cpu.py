@@ -298,3 +298,64 @@ def test_sampled_workspace_size(B, D, V):
     need = B * (2 * D + 1) * chunks * 16          # (max, fp64 sum) per chunk of every row
     assert sv.spec_accept_sampled_workspace_size(B, D, V) == need
     assert call_sampled(B, D, V, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
+
+
+def test_append_struct_layout_matches_c(tmp_path):
+    prog = tmp_path / "layout_append.c"
+    prog.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "spec_verify.h"\n'
+                    "int main(void){printf(\"%zu\", sizeof(sv_append_params));"
+                    + "".join(f'printf(" %zu", offsetof(sv_append_params, {f}));'
+                              for f, _ in sv.SvAppendParams._fields_)
+                    + "return 0;}\n")
+    exe = tmp_path / "layout_append"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(prog), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(sv.SvAppendParams)
+    assert vals[1:] == [getattr(sv.SvAppendParams, f).offset for f, _ in sv.SvAppendParams._fields_]
+
+
+def call_append(fp8=False, **kw):
+    ptrs = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=FAKE if fp8 else None,
+                vs=FAKE if fp8 else None, bt=FAKE, kli=FAKE, klo=FAKE)
+    shape = dict(batch=4, num_new=16, num_kv_heads=8, head_dim=128, max_blocks_per_seq=64,
+                 num_blocks=256, kv_dtype=sv.SV_KV_FP8_E4M3 if fp8 else sv.SV_KV_BF16)
+    for k, v in kw.items():
+        (ptrs if k in ptrs else shape)[k] = v
+    p = sv.make_append_params(**shape)
+    return sv.library().spec_kv_append(ctypes.byref(p), ptrs["kn"], ptrs["vn"], ptrs["kc"],
+                                       ptrs["vc"], ptrs["ks"], ptrs["vs"], ptrs["bt"], ptrs["kli"],
+                                       ptrs["klo"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), sv.SV_ERR_INVALID), (dict(num_new=0), sv.SV_ERR_INVALID),
+    (dict(num_kv_heads=0), sv.SV_ERR_INVALID), (dict(head_dim=96), sv.SV_ERR_UNSUPPORTED),
+    (dict(block_size=32), sv.SV_ERR_UNSUPPORTED), (dict(kv_dtype=5), sv.SV_ERR_INVALID),
+    (dict(num_blocks=0), sv.SV_ERR_INVALID), (dict(max_blocks_per_seq=0), sv.SV_ERR_INVALID),
+    (dict(max_blocks_per_seq=1 << 27), sv.SV_ERR_INVALID),
+    (dict(num_new=64 * 16 + 1), sv.SV_ERR_INVALID),
+    (dict(kn=None), sv.SV_ERR_INVALID), (dict(vn=None), sv.SV_ERR_INVALID),
+    (dict(kc=None), sv.SV_ERR_INVALID), (dict(vc=None), sv.SV_ERR_INVALID),
+    (dict(bt=None), sv.SV_ERR_INVALID), (dict(kli=None), sv.SV_ERR_INVALID),
+    (dict(klo=None), sv.SV_ERR_INVALID), (dict(kn=FAKE + 8), sv.SV_ERR_INVALID),
+    (dict(vc=FAKE + 4), sv.SV_ERR_INVALID), (dict(bt=FAKE + 2), sv.SV_ERR_INVALID),
+    (dict(klo=FAKE + 1), sv.SV_ERR_INVALID), (dict(ks=FAKE), sv.SV_ERR_INVALID),
+])
+def test_append_errors_bf16(kw, status):
+    assert call_append(**kw) == status
+    assert sv.last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(ks=None), dict(vs=None), dict(ks=FAKE + 2)])
+def test_append_errors_fp8(kw):
+    assert call_append(fp8=True, **kw) == sv.SV_ERR_INVALID
+
+
+def test_append_binding_raises():
+    p = sv.make_append_params(batch=0, num_new=1, num_kv_heads=1, head_dim=64,
+                              max_blocks_per_seq=1, num_blocks=1)
+    with pytest.raises(sv.SvError) as e:
+        sv.spec_kv_append(p, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == sv.SV_ERR_INVALID

@@ -241,13 +241,14 @@ class AppendInputs:
     v_new: np.ndarray
 
 
-def make_append_inputs(w: Workload, gains=(1.0,)) -> AppendInputs:
+def make_append_inputs(w: Workload, gains=(1.0,), base: Optional[AttnInputs] = None) -> AppendInputs:
     """The cache of ``make_attn_inputs(w)`` with its committed length set to the
     context T_b (the R positions after it are overwritten by the append), and new
     K/V rows N(0,1) * g, g drawn per (sequence, KV head) from ``gains`` (gains
     above 1 make appended values outgrow a block's e4m3 scale).
-    Streams: SeedSequence([seed, 3]).spawn(3) in the order k, v, gain."""
-    base = make_attn_inputs(w)
+    Streams: SeedSequence([seed, 3]).spawn(3) in the order k, v, gain.  ``base``:
+    the already drawn ``make_attn_inputs(w)``, to avoid drawing it again."""
+    base = make_attn_inputs(w) if base is None else base
     ss = np.random.SeedSequence([w.seed, 3]).spawn(3)
     rk, rv, rg = (np.random.default_rng(s) for s in ss)
     g = np.asarray(gains, dtype=np.float32)[rg.integers(0, len(gains), size=(w.B, 1, w.H_kv, 1))]
