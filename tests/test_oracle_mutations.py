@@ -173,3 +173,38 @@ def test_append_at_wrong_position_is_caught(monkeypatch):
                         lambda kn, vn, kc, vc, ks, vs, t, lens, fp8:
                         real(kn, vn, kc, vc, ks, vs, t, np.asarray(lens) + 1, fp8))
     _expect_pin_failure(T_app.test_bf16_rows_land_where_the_attention_gather_reads_them)
+
+
+import oracle.draft_signals as dsg  # noqa: E402
+from tests import test_oracle_draft_signals as T_dsg  # noqa: E402
+
+
+def test_entropy_in_bits_is_caught(monkeypatch):
+    real = dsg.oracle_signals
+    monkeypatch.setattr(T_dsg, "oracle_signals",
+                        lambda z, tau=1.0: (real(z, tau)[0], real(z, tau)[1] / np.log(2)))
+    _expect_pin_failure(T_dsg.test_signals_match_scipy, 1.0)
+
+
+def test_ties_to_longer_draft_are_caught(monkeypatch):
+    real = dsg.choose_draft_len
+
+    def longer(c, Dmax, rho, G):
+        d = real(c, Dmax, rho, G)
+        return max(dsg.candidate_lengths(Dmax, G)) if c == 0.0 and rho == 0.0 else d
+    monkeypatch.setattr(T_dsg, "choose_draft_len", longer)
+    _expect_pin_failure(T_dsg.test_choice_special_cases)
+
+
+def test_tile_rule_off_by_one_is_caught(monkeypatch):
+    def loose(Dmax, G):
+        return [D for D in range(Dmax + 1)
+                if not (G > 0 and G * D > 128 and (G * (D + 1)) % 128 != 0)]
+    monkeypatch.setattr(T_dsg, "candidate_lengths", loose)
+    _expect_pin_failure(T_dsg.test_tile_rule_candidates)
+
+
+def test_objective_without_draft_cost_is_caught(monkeypatch):
+    real = dsg.choose_draft_len
+    monkeypatch.setattr(T_dsg, "choose_draft_len", lambda c, Dmax, rho, G: real(c, Dmax, 0.0, G))
+    _expect_pin_failure(T_dsg.test_choice_matches_brute_force_grid)
