@@ -160,9 +160,41 @@ def time_accept_sampled(w, da, stream, sv, calls=20):
     us_call = ev[0].elapsed_time(ev[1]) * 1e3 / calls
     # every target and draft logit once, plus the one row each sequence draws from
     moved = (B * (2 * D + 1) * V + B * V) * 4
-    return {"kernels": "sv_sample_stats + sv_sample_decide", "avg_launch_us": round(us_call, 2),
+    return {"kernels": "sv_sample_stats + sv_sample_keep + sv_sample_chunk_sums + sv_sample_draw", "avg_launch_us": round(us_call, 2),
             "algorithmic_bytes": moved, "GBps": round(moved / (us_call * 1e-6) / 1e9, 1),
             "sum_accept_len": int(al.cpu().sum())}
+
+
+def time_draft_signals(w, stream, sv, calls=20):
+    """spec_draft_signals over one draft-model row per sequence ([B][V] fp32), the
+    signals and the next draft length (max_draft_len = D, rho = 0.05, G of the
+    workload), timed with HIP events after the step's own timing."""
+    import torch
+    from tests.gpu_util import dev
+    from workloads import make_draft_logits
+    z = dev(make_draft_logits(w.B, w.V, seed=w.seed))
+    conf = torch.empty((w.B,), dtype=torch.float32, device="cuda")
+    ent = torch.empty_like(conf)
+    nd = torch.empty((w.B,), dtype=torch.int32, device="cuda")
+    ws_bytes = sv.spec_draft_signals_workspace_size(w.B, w.V)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sh = stream.cuda_stream
+
+    def call():
+        sv.spec_draft_signals(w.B, w.V, 1.0, z, conf, ent, nd, w.D, 0.05, w.G, ws, ws_bytes,
+                              stream=sh)
+    call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(calls):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us_call = ev[0].elapsed_time(ev[1]) * 1e3 / calls
+    moved = w.B * w.V * 4
+    return {"kernels": "sv_draft_stats + sv_draft_decide", "avg_launch_us": round(us_call, 2),
+            "algorithmic_bytes": moved, "GBps": round(moved / (us_call * 1e-6) / 1e9, 1),
+            "next_draft_len_hist": np.bincount(nd.cpu().numpy(), minlength=w.D + 1).tolist()}
 
 
 def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
@@ -295,6 +327,7 @@ def main():
 
     append = time_append(w, da, stream, sv)
     sampled = time_accept_sampled(w, da, stream, sv)
+    signals = time_draft_signals(w, stream, sv)
 
     ms_per_step = total_ms / args.steps
     value = tokens_timed / (total_ms / 1e3)
@@ -345,6 +378,7 @@ def main():
                    "GBps": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9, 1)},
         "append": append,
         "accept_sampled": sampled,
+        "draft_signals": signals,
         "sum_accept_len_per_step": round(tokens_timed / args.steps, 2),
         "kernel_src_sha": src_hash,
         "input_gen_s": round(t_gen, 1),

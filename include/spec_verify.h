@@ -19,6 +19,8 @@
  *                      committed KV length.
  *   spec_accept_sampled  the same for sampled decoding: lossless stochastic
  *                      acceptance of the drafts and a draw of the next token.
+ *   spec_draft_signals confidence and entropy of the draft's distribution and
+ *                      the draft length for the next step.
  *
  * Where the operations are defined (the pages this library implements):
  *   - one target pass over the drafted positions plus the bonus position, and
@@ -289,6 +291,51 @@ sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const voi
                          void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                          const int32_t* block_table, const int32_t* kv_lens_in,
                          int32_t* kv_lens_out, void* stream);
+
+/* Bytes of device workspace spec_draft_signals needs for (rows, vocab). */
+sv_status spec_draft_signals_workspace_size(int32_t rows, int32_t vocab, size_t* bytes);
+
+/*
+ * Draft-side signals and the next draft length.  The confidence (largest
+ * probability) and entropy of the draft model's next-token distribution predict
+ * how many drafts the target accepts (SpecKV summary, arXiv 2605.02888, section
+ * "Technical core"); the next draft length maximises expected tokens per unit
+ * time with the expected-token formula of "GPU and LLM" ch. 5, section
+ * "Speculative decoding (2)", and the drafting cost of the NVIDIA co-design
+ * summary, guidelines 3 and 4.
+ *
+ * For row r, p = softmax(draft_logits[r] / temperature):
+ *     confidence[r] = max_v p_v
+ *     entropy[r]    = -sum_v p_v ln p_v            (nats)
+ *     next_draft_len[r] = the D in the candidates maximising
+ *         f(D) = E(a, D) / (1 + rho D),  E(a, D) = sum_{i=0..D} a^i,  a = min(confidence[r], 1)
+ *     (ties to the shorter D).  Candidates: 0 .. max_draft_len; with
+ *     group_size G > 0, a D with G (1 + D) > 128 only if G (1 + D) is a multiple
+ *     of 128 (whole 128-row attention tiles).  f is evaluated in fp64 from the
+ *     returned fp32 confidence, in this order and without fused operations:
+ *     P_0 = 1, P_{D+1} = P_D * a; E = D + 1 if a == 1 else (1 - P_{D+1}) / (1 - a);
+ *     cost = 1 + (rho * D); f = E / cost.
+ * The GPU sums fp32 exponentials in fp64: confidence and entropy are within
+ * about 1e-6 relative of exact values.
+ *
+ *   draft_logits    [rows][V] fp32, 16-byte aligned.  Finite or -inf, at least
+ *                   one finite value per row.
+ *   confidence,     [rows] fp32, written.
+ *   entropy
+ *   next_draft_len  [rows] int32, written; may be NULL (signals only).
+ *   max_draft_len   in [0, 63];  rho >= 0 (draft cost per drafted token relative
+ *                   to one target pass);  group_size G in [0, 1024], 0 = no tile rule.
+ *   workspace       at least spec_draft_signals_workspace_size() bytes,
+ *                   256-byte aligned.
+ * Errors: SV_ERR_INVALID for rows outside [1, 65535], vocab < 1, temperature,
+ * max_draft_len, rho or group_size out of range, NULL or misaligned pointers;
+ * SV_ERR_WORKSPACE.
+ */
+sv_status spec_draft_signals(int32_t rows, int32_t vocab, float temperature,
+                             const float* draft_logits, float* confidence, float* entropy,
+                             int32_t* next_draft_len, int32_t max_draft_len, float rho,
+                             int32_t group_size, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* sv_status_string(sv_status s);

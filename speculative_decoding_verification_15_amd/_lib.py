@@ -20,7 +20,8 @@ SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1
 # Every symbol include/spec_verify.h declares.
 EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_workspace_size",
            "spec_accept", "spec_accept_sampled_workspace_size", "spec_accept_sampled",
-           "spec_kv_append", "sv_status_string", "sv_last_error", "sv_abi_version")
+           "spec_kv_append", "spec_draft_signals_workspace_size", "spec_draft_signals",
+           "sv_status_string", "sv_last_error", "sv_abi_version")
 
 
 class SvAttnParams(ctypes.Structure):
@@ -83,6 +84,11 @@ def _load():
     lib.spec_accept_sampled.restype = U
     lib.spec_kv_append.argtypes = [ctypes.POINTER(SvAppendParams)] + [P] * 10
     lib.spec_kv_append.restype = U
+    lib.spec_draft_signals_workspace_size.argtypes = [I32, I32, ctypes.POINTER(S)]
+    lib.spec_draft_signals_workspace_size.restype = U
+    lib.spec_draft_signals.argtypes = [I32, I32, ctypes.c_float, P, P, P, P, I32, ctypes.c_float,
+                                       I32, P, S, P]
+    lib.spec_draft_signals.restype = U
     lib.sv_status_string.argtypes = [U]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -206,3 +212,21 @@ def spec_kv_append(params: SvAppendParams, k_new, v_new, k_cache, v_cache, k_sca
     _check(_lib.spec_kv_append(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
                                _ptr(kv_lens_in), _ptr(kv_lens_out), _stream(stream)))
+
+
+def spec_draft_signals_workspace_size(rows: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.spec_draft_signals_workspace_size(rows, vocab, ctypes.byref(n)))
+    return int(n.value)
+
+
+def spec_draft_signals(rows, vocab, temperature, draft_logits, confidence, entropy, next_draft_len,
+                       max_draft_len, rho, group_size, workspace, workspace_bytes=None,
+                       stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(_lib.spec_draft_signals(rows, vocab, float(temperature), _ptr(draft_logits),
+                                   _ptr(confidence), _ptr(entropy), _ptr(next_draft_len),
+                                   int(max_draft_len), float(rho), int(group_size),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -280,6 +280,56 @@ sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const voi
   return SV_OK;
 }
 
+static sv_status check_draft_signals(int32_t rows, int32_t vocab, float temperature,
+                                     int32_t max_draft_len, float rho, int32_t group_size) {
+  if (rows < 1 || rows > kMaxGridYZ)
+    return fail(SV_ERR_INVALID, "rows must be in [1, %d] (got %d)", kMaxGridYZ, rows);
+  if (vocab < 1) return fail(SV_ERR_INVALID, "vocab must be >= 1 (got %d)", vocab);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SV_ERR_INVALID, "temperature must be finite and > 0");
+  if (max_draft_len < 0 || max_draft_len > kMaxDraft)
+    return fail(SV_ERR_INVALID, "max_draft_len must be in [0, %d] (got %d)", kMaxDraft,
+                max_draft_len);
+  if (!(rho >= 0.f) || !std::isfinite(rho)) return fail(SV_ERR_INVALID, "rho must be finite and >= 0");
+  if (group_size < 0 || group_size > 1024)
+    return fail(SV_ERR_INVALID, "group_size must be in [0, 1024] (got %d)", group_size);
+  return SV_OK;
+}
+
+sv_status spec_draft_signals_workspace_size(int32_t rows, int32_t vocab, size_t* bytes) {
+  if (!bytes) return fail(SV_ERR_INVALID, "bytes is NULL");
+  sv_status s = check_draft_signals(rows, vocab, 1.f, 0, 0.f, 0);
+  if (s != SV_OK) return s;
+  *bytes = sv::draft_signals_workspace_bytes(rows, vocab);
+  return SV_OK;
+}
+
+sv_status spec_draft_signals(int32_t rows, int32_t vocab, float temperature,
+                             const float* draft_logits, float* confidence, float* entropy,
+                             int32_t* next_draft_len, int32_t max_draft_len, float rho,
+                             int32_t group_size, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  sv_status s = check_draft_signals(rows, vocab, temperature, max_draft_len, rho, group_size);
+  if (s != SV_OK) return s;
+  if (!draft_logits || !confidence || !entropy)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned(draft_logits, 16)) return fail(SV_ERR_INVALID, "draft_logits must be 16-byte aligned");
+  if (!aligned(confidence, 4) || !aligned(entropy, 4) ||
+      (next_draft_len && !aligned(next_draft_len, 4)))
+    return fail(SV_ERR_INVALID, "output arrays must be 4-byte aligned");
+  const size_t need = sv::draft_signals_workspace_bytes(rows, vocab);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(SV_ERR_INVALID, "workspace must be 256-byte aligned");
+  hipError_t e = sv::launch_draft_signals(rows, vocab, temperature, draft_logits, confidence,
+                                          entropy, next_draft_len, max_draft_len, rho, group_size,
+                                          workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
 const char* sv_status_string(sv_status s) {
   switch (s) {
     case SV_OK: return "SV_OK";

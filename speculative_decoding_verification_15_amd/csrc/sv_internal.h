@@ -25,9 +25,11 @@ hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t
                          const int32_t* kv_in, int32_t* kv_out, void* ws, hipStream_t stream);
 
 // Stochastic acceptance: one (max, fp64 sum) record of 16 bytes per 4096-logit
-// chunk of every target row (B (1 + D)) and draft row (B D).
+// chunk of every target row (B (1 + D)) and draft row (B D); a 32-byte draw
+// record per sequence; two fp64 weight sums per chunk of each sequence's drawn row.
 inline size_t accept_sampled_workspace_bytes(int B, int D, int V) {
-  return (size_t)B * (size_t)(2 * D + 1) * (size_t)argmax_chunks(V) * 16u;
+  const size_t chunks = (size_t)argmax_chunks(V);
+  return (size_t)B * (size_t)(2 * D + 1) * chunks * 16u + (size_t)B * 32u + (size_t)B * chunks * 16u;
 }
 
 hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt, const float* zd,
@@ -35,6 +37,13 @@ hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt
                                  const float* u_sample, int32_t* accept_len, int32_t* out_tokens,
                                  const int32_t* kv_in, int32_t* kv_out, void* ws,
                                  hipStream_t stream);
+
+// Draft signals (sv_draft.hip): one 32-byte record per 4096-logit chunk of every row.
+size_t draft_signals_workspace_bytes(int rows, int V);
+hipError_t launch_draft_signals(int rows, int V, float tau, const float* logits,
+                                float* confidence, float* entropy, int32_t* next_len,
+                                int max_draft_len, float rho, int G, void* ws,
+                                hipStream_t stream);
 
 // KV append (sv_append.hip): one workgroup per sequence.
 struct AppendPlan {

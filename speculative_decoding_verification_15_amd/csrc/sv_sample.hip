@@ -18,12 +18,16 @@
 // correctly rounded division and the accurate exponential, so its error is a
 // few ulp and independent from one logit to the next: a rounded log2(e) / tau
 // would scale every exponent by the same factor and shift all the draw's
-// boundaries the same way.  Pass 2
-// (sv_sample_decide, one workgroup per sequence) combines the chunks of its
-// rows, runs the keep tests in order, and draws the emitted token from the one
-// row it needs: a first pass sums the weights of each thread's contiguous
-// segment (fp64), an exclusive scan places the segments, and the thread whose
-// segment holds u * total walks it again to find the index.
+// boundaries the same way.
+// Pass 2 (sv_sample_keep, one workgroup per sequence) combines the chunks of its
+// rows, runs the keep tests in order and writes every output but the emitted
+// token.  The emitted token is drawn from the one row it needs in two passes
+// that read it coalesced: sv_sample_chunk_sums (one workgroup per 4096-logit
+// chunk) sums the weights of each chunk in fp64; sv_sample_draw (one workgroup
+// per sequence) finds the chunk holding u * total from the chunk sums in index
+// order, sums 16 consecutive weights per thread inside it, places the threads'
+// segments by an exclusive prefix in thread order, and the thread whose segment
+// holds the target walks it again to find the index.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -110,26 +114,47 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_stats(
   }
 }
 
-// grid = B, 256 threads.
-__global__ __launch_bounds__(kArgmaxThreads) void sv_sample_decide(
+// What the draw of sequence b needs, written by sv_sample_keep.
+struct DrawInfo {
+  int32_t n;       // first draft not kept (D if all kept): the emitted token's row
+  int32_t resid;   // 1: draw from max(0, p_n - q_n); 0: draw from p_n (= p_D)
+  float Mp, Mq;    // row maxima of target row n and draft row n
+  double invSp;    // 1 / S of target row n
+  double invSq;    // 1 / S of draft row n (resid only)
+};
+
+// The unnormalised weights of the emitted token's distribution at index v:
+// p_n(v), and max(0, p_n(v) - q_n(v)) when drawing from the residual.  fp32
+// exponentials (correctly rounded division, accurate exp) times an fp64 1 / S:
+// a rounded fp32 1 / S would scale all of p, or all of q, by one factor and move
+// every boundary of the residual together.
+__device__ __forceinline__ double weight_p(float z, const DrawInfo& d, float tau) {
+  return (double)expf((z - d.Mp) / tau) * d.invSp;
+}
+__device__ __forceinline__ double weight_r(float z, float y, const DrawInfo& d, float tau) {
+  const double q = (double)expf((y - d.Mq) / tau) * d.invSq;
+  return fmax(weight_p(z, d, tau) - q, 0.0);
+}
+
+// grid = B, 256 threads: row normalisers (max M over the chunks and
+// S = sum_c s_c e^((m_c - M) / tau)), the keep tests in order, and every output
+// but the emitted token.
+__global__ __launch_bounds__(kArgmaxThreads) void sv_sample_keep(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ draft,
-    const float* __restrict__ u_accept, const float* __restrict__ u_sample, int D, int V,
-    int chunks, float tau, const SampleStat* __restrict__ st, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ out_tokens, const int32_t* __restrict__ kv_in,
-    int32_t* __restrict__ kv_out) {
+    const float* __restrict__ u_accept, int D, int V, int chunks, float tau,
+    const SampleStat* __restrict__ st, DrawInfo* __restrict__ info,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
+    const int32_t* __restrict__ kv_in, int32_t* __restrict__ kv_out) {
   constexpr int kThreads = kArgmaxThreads;
   __shared__ float s_M[2 * 64 + 1];         // per row r: target rows 0 .. D, draft rows R + j
   __shared__ double s_S[2 * 64 + 1];
-  __shared__ double s_part[kThreads];       // segment sums, then their exclusive prefixes
-  __shared__ double s_total;
-  __shared__ int s_n, s_tok;
+  __shared__ bool s_keep[64];
   const int b = blockIdx.x;
   const int R = D + 1;
   const int t = threadIdx.x;
   const int lane = t % kWave, wave = t / kWave;
   const int B = gridDim.x;
 
-  // Row normalisers: max M over the chunks and S = sum_c s_c e^((m_c - M) / tau).
   for (int r = wave; r < R + D; r += kThreads / kWave) {
     const size_t row = r < R ? (size_t)b * R + r : (size_t)B * R + (size_t)b * D + (r - R);
     const SampleStat* sr = st + row * chunks;
@@ -148,80 +173,191 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_decide(
       s_S[r] = sc;
     }
   }
-  if (t == 0) s_tok = -1;
   __syncthreads();
+  // every keep test's inputs fetched at once (thread j: draft j), tested in order below
+  if (t < D) {
+    const int j = t;
+    const int d = min(max(draft[(size_t)b * D + j], 0), V - 1);
+    const double p = (double)expf((zt[((size_t)b * R + j) * V + d] - s_M[j]) / tau) / s_S[j];
+    const double q = (double)expf((zd[((size_t)b * D + j) * V + d] - s_M[R + j]) / tau) / s_S[R + j];
+    s_keep[j] = (double)u_accept[(size_t)b * D + j] * q < p;
+  }
+  __syncthreads();
+  if (t != 0) return;
+  int n = D;
+  for (int j = 0; j < D; ++j) {
+    if (!s_keep[j]) {
+      n = j;
+      break;
+    }
+  }
+  const bool resid = n < D;
+  info[b] = DrawInfo{n, resid ? 1 : 0, s_M[n], resid ? s_M[R + n] : 0.f, 1.0 / s_S[n],
+                     resid ? 1.0 / s_S[R + n] : 0.0};
+  accept_len[b] = n + 1;
+  const int k = kv_in[b];
+  kv_out[b] = k - R + n + 1;
+  for (int j = 0; j < R; ++j)
+    if (j != n) out_tokens[(size_t)b * R + j] = j < n ? draft[(size_t)b * D + j] : -1;
+}
 
-  // Keep tests, in order, up to the first draft not kept.
+// grid = (chunks, B), 256 threads: the sums of the draw weights over each
+// 4096-logit chunk of the emitted token's row, read coalesced.  Per chunk:
+// {sum of the drawn weights, sum of p_n} (the second serves when the residual is
+// zero everywhere, p_n == q_n).
+template <bool VEC>
+__global__ __launch_bounds__(kArgmaxThreads) void sv_sample_chunk_sums(
+    const float* __restrict__ zt, const float* __restrict__ zd, int D, int V, int chunks,
+    float tau, const DrawInfo* __restrict__ info, double2* __restrict__ sums) {
+  constexpr int U = kArgmaxChunk / kArgmaxThreads;
+  __shared__ double red_w[kArgmaxThreads / kWave], red_p[kArgmaxThreads / kWave];
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const int R = D + 1;
+  const DrawInfo di = info[b];
+  const float* zr = zt + ((size_t)b * R + di.n) * V;
+  const float* yr = di.resid ? zd + ((size_t)b * D + di.n) * V : zr;
+  const int base = chunk * kArgmaxChunk;
+  const int t = threadIdx.x;
+  double sw = 0.0, sp = 0.0;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int u = 0; u < U / 4; ++u) {
+      const int i0 = base + (u * kArgmaxThreads + t) * 4;
+      if (i0 >= V) continue;
+      f32x4 z4, y4;
+      if (i0 + 3 < V) {
+        z4 = *reinterpret_cast<const f32x4*>(zr + i0);
+        y4 = *reinterpret_cast<const f32x4*>(yr + i0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z4[e] = (i0 + e < V) ? zr[i0 + e] : -INFINITY;
+          y4[e] = (i0 + e < V) ? yr[i0 + e] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (z4[e] == -INFINITY) continue;
+        const double p = weight_p(z4[e], di, tau);
+        sp += p;
+        sw += di.resid ? weight_r(z4[e], y4[e], di, tau) : p;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * kArgmaxThreads + t;
+      if (i >= V || zr[i] == -INFINITY) continue;
+      const double p = weight_p(zr[i], di, tau);
+      sp += p;
+      sw += di.resid ? weight_r(zr[i], yr[i], di, tau) : p;
+    }
+  }
+  sw = wave_sum(sw);
+  sp = wave_sum(sp);
+  if (t % kWave == 0) {
+    red_w[t / kWave] = sw;
+    red_p[t / kWave] = sp;
+  }
+  __syncthreads();
   if (t == 0) {
-    int n = D;
-    for (int j = 0; j < D; ++j) {
-      const int d = min(max(draft[(size_t)b * D + j], 0), V - 1);
-      const double p = (double)expf((zt[((size_t)b * R + j) * V + d] - s_M[j]) / tau) / s_S[j];
-      const double q =
-          (double)expf((zd[((size_t)b * D + j) * V + d] - s_M[R + j]) / tau) / s_S[R + j];
-      if (!((double)u_accept[(size_t)b * D + j] * q < p)) {
-        n = j;
-        break;
-      }
+    double a = red_w[0], c = red_p[0];
+#pragma unroll
+    for (int i = 1; i < kArgmaxThreads / kWave; ++i) {
+      a += red_w[i];
+      c += red_p[i];
     }
-    s_n = n;
+    sums[(size_t)b * chunks + chunk] = double2{a, c};
+  }
+}
+
+// grid = B, 256 threads: the chunk holding u * total (chunk sums in index
+// order), then inside it 16 consecutive logits per thread: thread sums, their
+// exclusive prefix in thread order, and a walk by the thread whose segment holds
+// the target.  Should rounding keep every running sum short of the target, the
+// last positive weight in reach is taken.
+__global__ __launch_bounds__(kArgmaxThreads) void sv_sample_draw(
+    const float* __restrict__ zt, const float* __restrict__ zd, const float* __restrict__ u_sample,
+    int D, int V, int chunks, float tau, const DrawInfo* __restrict__ info,
+    const double2* __restrict__ sums, int32_t* __restrict__ out_tokens) {
+  constexpr int kThreads = kArgmaxThreads;
+  constexpr int kPer = kArgmaxChunk / kThreads;      // 16 logits per thread
+  __shared__ double s_own[kThreads], s_part[kThreads];
+  __shared__ double s_off;
+  __shared__ int s_chunk, s_tok, s_resid, s_sel;
+  const int b = blockIdx.x;
+  const int R = D + 1;
+  const int t = threadIdx.x;
+  DrawInfo di = info[b];
+  if (t == 0) {
+    const double2* sb = sums + (size_t)b * chunks;
+    double tot_w = 0.0;
+    for (int c = 0; c < chunks; ++c) tot_w += sb[c].x;
+    const bool use_w = !(di.resid && tot_w == 0.0);   // p_n == q_n: draw from p_n
+    double total = 0.0;
+    for (int c = 0; c < chunks; ++c) total += use_w ? sb[c].x : sb[c].y;
+    const double T = (double)u_sample[b] * total;
+    double run = 0.0;
+    int pick = -1, last = 0;
+    double off = 0.0, last_off = 0.0;
+    for (int c = 0; c < chunks; ++c) {
+      const double w = use_w ? sb[c].x : sb[c].y;
+      if (w > 0.0) {
+        last = c;
+        last_off = run;
+        if (T < run + w) {
+          pick = c;
+          off = run;
+          break;
+        }
+      }
+      run += w;
+    }
+    s_chunk = pick >= 0 ? pick : last;
+    s_off = T - (pick >= 0 ? off : last_off);          // target inside the chunk
+    s_resid = use_w ? di.resid : 0;
+    s_tok = -1;
   }
   __syncthreads();
-  const int n = s_n;
-
-  // The row to draw from: the residual max(0, p_n - q_n) after a draft not
-  // kept, else p_D; a residual that is zero everywhere falls back to p_n.
-  const float* zr = zt + ((size_t)b * R + n) * V;
-  const float Mp = s_M[n];
-  // Weights in fp64 (fp32 exponentials times fp64 1 / S): a rounded fp32 1 / S
-  // would scale all of p, or all of q, by one factor and move every boundary of
-  // the residual together.
-  const double invSp = 1.0 / s_S[n];
-  bool resid = n < D;
-  const float* yr = resid ? zd + ((size_t)b * D + n) * V : zr;
-  const float Mq = resid ? s_M[R + n] : 0.f;
-  const double invSq = resid ? 1.0 / s_S[R + n] : 0.0;
+  di.resid = s_resid;
+  const int chunk = s_chunk;
+  const double Tc = s_off;
+  const float* zr = zt + ((size_t)b * R + di.n) * V;
+  const float* yr = di.resid ? zd + ((size_t)b * D + di.n) * V : zr;
+  const int v0 = min(chunk * kArgmaxChunk + t * kPer, V), v1 = min(v0 + kPer, V);
   auto weight = [&](int v) -> double {
-    const double p = (double)expf((zr[v] - Mp) / tau) * invSp;
-    if (!resid) return p;
-    const double q = (double)expf((yr[v] - Mq) / tau) * invSq;
-    return fmax(p - q, 0.0);
+    if (zr[v] == -INFINITY) return 0.0;
+    return di.resid ? weight_r(zr[v], yr[v], di, tau) : weight_p(zr[v], di, tau);
   };
-  const int seg = (V + kThreads - 1) / kThreads;
-  const int v0 = min(t * seg, V), v1 = min(v0 + seg, V);
-  double own = 0.0, pre = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    own = 0.0;
-    for (int v = v0; v < v1; ++v) own += weight(v);
-    s_part[t] = own;
-    __syncthreads();
-    if (t == 0) {                            // exclusive prefix, in thread order
-      double run = 0.0;
-      for (int i = 0; i < kThreads; ++i) {
-        const double x = s_part[i];
-        s_part[i] = run;
-        run += x;
+  double own = 0.0;
+  for (int v = v0; v < v1; ++v) own += weight(v);
+  s_own[t] = own;
+  __syncthreads();
+  if (t == 0) {
+    // exclusive prefix in thread order; the first segment with weight whose end
+    // passes Tc holds it (else the last segment with weight)
+    double run = 0.0;
+    int sel = -1, last = -1;
+    for (int i = 0; i < kThreads; ++i) {
+      const double x = s_own[i];
+      s_part[i] = run;
+      if (x > 0.0) {
+        last = i;
+        if (sel < 0 && Tc < run + x) sel = i;
       }
-      s_total = run;
+      run += x;
     }
-    __syncthreads();
-    pre = s_part[t];
-    if (!(resid && s_total == 0.0)) break;   // uniform: s_total is shared
-    resid = false;                           // p_n == q_n: draw from p_n
-    __syncthreads();                         // everyone has read s_part / s_total
+    s_sel = sel >= 0 ? sel : last;
   }
-  const double T = (double)u_sample[b] * s_total;
-  // The segments tile [0, total) in thread order; exactly one with own > 0
-  // holds T.  Its walk repeats the same weights; should rounding keep the
-  // running sum from passing T, the segment's last positive weight is taken.
-  if (own > 0.0 && pre <= T && T < pre + own) {
-    double run = pre;
+  __syncthreads();
+  if (t == s_sel) {
+    double run = s_part[t];
     int tok = -1, last = -1;
     for (int v = v0; v < v1; ++v) {
       const double w = weight(v);
       if (w > 0.0) last = v;
       run += w;
-      if (run > T) {
+      if (run > Tc) {
         tok = v;
         break;
       }
@@ -229,13 +365,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_decide(
     s_tok = tok >= 0 ? tok : last;
   }
   __syncthreads();
-  if (t == 0) {
-    const int tok = s_tok;
-    accept_len[b] = n + 1;
-    kv_out[b] = kv_in[b] - R + n + 1;
-    for (int j = 0; j < R; ++j)
-      out_tokens[(size_t)b * R + j] = j < n ? draft[(size_t)b * D + j] : (j == n ? tok : -1);
-  }
+  if (t == 0) out_tokens[(size_t)b * R + di.n] = s_tok >= 0 ? s_tok : chunk * kArgmaxChunk;
 }
 
 hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt, const float* zd,
@@ -253,9 +383,25 @@ hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt
     sv_sample_stats<false><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sv_sample_decide<<<B, kArgmaxThreads, 0, stream>>>(zt, zd, draft, u_accept, u_sample, D, V,
-                                                     chunks, tau, st, accept_len, out_tokens,
-                                                     kv_in, kv_out);
+  // workspace after the chunk statistics: DrawInfo[B], then {sum w, sum p}[B][chunks]
+  const size_t st_bytes = (size_t)B * (R + D) * chunks * sizeof(SampleStat);
+  auto* info = reinterpret_cast<DrawInfo*>(static_cast<char*>(ws) + st_bytes);
+  auto* sums = reinterpret_cast<double2*>(static_cast<char*>(ws) + st_bytes + (size_t)B * sizeof(DrawInfo));
+  sv_sample_keep<<<B, kArgmaxThreads, 0, stream>>>(zt, zd, draft, u_accept, D, V, chunks, tau, st,
+                                                   info, accept_len, out_tokens, kv_in, kv_out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid3(chunks, B);
+  if (V % 4 == 0)
+    sv_sample_chunk_sums<true><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks, tau,
+                                                                     info, sums);
+  else
+    sv_sample_chunk_sums<false><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks, tau,
+                                                                      info, sums);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  sv_sample_draw<<<B, kArgmaxThreads, 0, stream>>>(zt, zd, u_sample, D, V, chunks, tau, info, sums,
+                                                   out_tokens);
   return hipGetLastError();
 }
 

@@ -296,6 +296,7 @@ def test_sampled_no_drafts_allows_null_draft_arrays():
 def test_sampled_workspace_size(B, D, V):
     chunks = -(-V // 4096)
     need = B * (2 * D + 1) * chunks * 16          # (max, fp64 sum) per chunk of every row
+    need += B * 32 + B * chunks * 16               # draw record; weight sums of the drawn row
     assert sv.spec_accept_sampled_workspace_size(B, D, V) == need
     assert call_sampled(B, D, V, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
 
@@ -359,3 +360,32 @@ def test_append_binding_raises():
     with pytest.raises(sv.SvError) as e:
         sv.spec_kv_append(p, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == sv.SV_ERR_INVALID
+
+
+def call_signals(rows=32, V=1000, tau=1.0, Dmax=15, rho=0.05, G=8, ws_bytes=1 << 40, **ptrs):
+    a = dict(z=FAKE, c=FAKE, h=FAKE, nd=FAKE, ws=FAKE * 4)
+    a.update(ptrs)
+    return sv.library().spec_draft_signals(rows, V, tau, a["z"], a["c"], a["h"], a["nd"], Dmax, rho,
+                                           G, a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=0), sv.SV_ERR_INVALID), (dict(rows=65536), sv.SV_ERR_INVALID),
+    (dict(V=0), sv.SV_ERR_INVALID), (dict(tau=0.0), sv.SV_ERR_INVALID),
+    (dict(tau=float("nan")), sv.SV_ERR_INVALID), (dict(Dmax=-1), sv.SV_ERR_INVALID),
+    (dict(Dmax=64), sv.SV_ERR_INVALID), (dict(rho=-0.1), sv.SV_ERR_INVALID),
+    (dict(rho=float("inf")), sv.SV_ERR_INVALID), (dict(G=-1), sv.SV_ERR_INVALID),
+    (dict(z=None), sv.SV_ERR_INVALID), (dict(c=None), sv.SV_ERR_INVALID),
+    (dict(h=None), sv.SV_ERR_INVALID), (dict(z=FAKE + 4), sv.SV_ERR_INVALID),
+    (dict(c=FAKE + 2), sv.SV_ERR_INVALID), (dict(nd=FAKE + 1), sv.SV_ERR_INVALID),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE), (dict(ws=FAKE + 64), sv.SV_ERR_INVALID),
+    (dict(ws_bytes=32 * 1 * 32 - 1), sv.SV_ERR_WORKSPACE),
+])
+def test_draft_signals_errors(kw, status):
+    assert call_signals(**kw) == status
+    assert sv.last_error() != ""
+
+
+@pytest.mark.parametrize("rows,V", [(1, 1), (32, 128256), (7, 4097), (65535, 10)])
+def test_draft_signals_workspace_size(rows, V):
+    assert sv.spec_draft_signals_workspace_size(rows, V) == rows * (-(-V // 4096)) * 32

@@ -256,3 +256,14 @@ def make_append_inputs(w: Workload, gains=(1.0,), base: Optional[AttnInputs] = N
     v = rv.standard_normal((w.B, w.R, w.H_kv, w.hd), dtype=np.float32) * g
     return AppendInputs(base=base, committed=(base.kv_lens - w.R).astype(np.int32),
                         k_new=f32_to_bf16_bits(k), v_new=f32_to_bf16_bits(v))
+
+
+def make_draft_logits(rows: int, V: int, seed: int, sharp=(0.3, 8.0)) -> np.ndarray:
+    """Draft-model logits [rows][V] fp32: N(0,1) times a per-row sharpness drawn
+    log-uniformly from ``sharp`` (so the rows' confidences span flat to peaked
+    distributions).  Streams: SeedSequence([seed, 4]).spawn(2) (logits, sharpness)."""
+    ss = np.random.SeedSequence([seed, 4]).spawn(2)
+    rz, rs = (np.random.default_rng(s) for s in ss)
+    z = rz.standard_normal((rows, V), dtype=np.float32)
+    s = np.exp(rs.uniform(np.log(sharp[0]), np.log(sharp[1]), size=(rows, 1))).astype(np.float32)
+    return np.ascontiguousarray(z * s, dtype=np.float32)
