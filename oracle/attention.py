@@ -92,12 +92,30 @@ def _visible(R: int, L: int) -> np.ndarray:
     return np.arange(L)[None, :] <= (P + np.arange(R))[:, None]
 
 
+def _visible_tree(parents, L: int) -> np.ndarray:
+    """visible[i, t] for draft-tree verification: new position j holds tree node
+    j (parent[j] < j, parent[0] = -1); node i sees every context key t < L - R
+    and the new keys of itself and its ancestors, found by walking parents."""
+    R = len(parents)
+    P = L - R
+    vis = np.zeros((R, L), dtype=bool)
+    vis[:, :P] = True
+    for i in range(R):
+        j = i
+        while j >= 0:
+            vis[i, P + j] = True
+            j = int(parents[j])
+    return vis
+
+
 def oracle_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, *,
-                D, H_kv, sm_scale, seqs=None, kv_heads=None):
+                D, H_kv, sm_scale, seqs=None, kv_heads=None, parents=None):
     """Full-softmax attention of the R = D + 1 verified positions.
 
-    Returns fp64 [B][R][H_q][hd]; rows outside ``seqs`` x ``kv_heads`` (when
-    given) are NaN.
+    With ``parents`` ([B][R] int, a draft tree per sequence) the new positions
+    are tree nodes and each sees its ancestors instead of every earlier
+    position (``_visible_tree``).  Returns fp64 [B][R][H_q][hd]; rows outside
+    ``seqs`` x ``kv_heads`` (when given) are NaN.
     """
     B, R, H_q, hd = q.shape
     assert R == D + 1 and H_q % H_kv == 0
@@ -111,7 +129,7 @@ def oracle_attn(q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, *,
         K, V = gather_kv(k_cache, v_cache, k_scale, v_scale, block_table, b, L,
                          None if kv_heads is None else list(kv_heads))
         Q = bf16_bits_to_f64(q[b])                     # [R][H_q][hd]
-        vis = _visible(R, L)
+        vis = _visible(R, L) if parents is None else _visible_tree(parents[b], L)
         for kvh in (range(H_kv) if kv_heads is None else kv_heads):
             for g in range(G):
                 h = kvh * G + g

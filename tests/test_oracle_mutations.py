@@ -208,3 +208,43 @@ def test_objective_without_draft_cost_is_caught(monkeypatch):
     real = dsg.choose_draft_len
     monkeypatch.setattr(T_dsg, "choose_draft_len", lambda c, Dmax, rho, G: real(c, Dmax, 0.0, G))
     _expect_pin_failure(T_dsg.test_choice_matches_brute_force_grid)
+
+
+import oracle.tree as otree  # noqa: E402
+from tests import test_oracle_tree as T_tree  # noqa: E402
+
+
+def test_tree_parent_only_visibility_is_caught(monkeypatch):
+    # node i sees itself and its parent, not the whole root path
+    def shallow(parents, L):
+        R = len(parents)
+        vis = np.zeros((R, L), dtype=bool)
+        vis[:, : L - R] = True
+        for i in range(R):
+            vis[i, L - R + i] = True
+            if parents[i] >= 0:
+                vis[i, L - R + int(parents[i])] = True
+        return vis
+    monkeypatch.setattr(att, "_visible_tree", shallow)
+    _expect_pin_failure(T_tree.test_tree_attention_matches_torch_sdpa)
+
+
+def test_tree_walk_takes_highest_child_is_caught(monkeypatch):
+    def highest(logits, tokens, parents, kv):
+        logits = np.asarray(logits, np.float32)
+        B, R, V = logits.shape
+        tgt = acc.oracle_argmax(logits)
+        out = otree.oracle_accept_tree(logits, tokens, parents, kv)
+        for b in range(B):
+            path = [0]
+            while True:
+                cs = [c for c in range(R - 1, path[-1], -1)
+                      if parents[b][c] == path[-1] and tokens[b][c] == tgt[b, path[-1]]]
+                if not cs:
+                    break
+                path.append(cs[0])
+            out["accept_path"][b, :] = -1
+            out["accept_path"][b, : len(path)] = path
+        return out
+    monkeypatch.setattr(T_tree, "oracle_accept_tree", highest)
+    _expect_pin_failure(T_tree.test_tree_acceptance_brute_force_small)

@@ -267,3 +267,56 @@ def make_draft_logits(rows: int, V: int, seed: int, sharp=(0.3, 8.0)) -> np.ndar
     z = rz.standard_normal((rows, V), dtype=np.float32)
     s = np.exp(rs.uniform(np.log(sharp[0]), np.log(sharp[1]), size=(rows, 1))).astype(np.float32)
     return np.ascontiguousarray(z * s, dtype=np.float32)
+
+
+@dataclasses.dataclass
+class TreePlan:
+    """A draft tree per sequence over the R new positions (node 0 = the root, the
+    last committed token; parents[b][j] < j), its ancestor masks in the layout
+    the tree attention reads, and the recipe for the node tokens."""
+    w: Workload
+    parents: np.ndarray         # [B][R] int32, parents[:, 0] = -1
+    masks: np.ndarray           # [B][R] uint64: bit j of masks[b][i] = j is i or an ancestor
+    match: np.ndarray           # [B][R] bool: node j carries its parent's target token
+    other: np.ndarray           # [B][R] uniform draws in [0, V-2]
+
+
+def make_tree_plan(w: Workload, shape: str = "random", width: int = 3,
+                   p_match: float = 0.6) -> TreePlan:
+    """Trees of R = 1 + D nodes: "random" (each node's parent drawn uniformly from
+    the ``width`` nodes before it), "chain" (parent j - 1), "star" (parent 0).
+    Streams: SeedSequence([seed, 5]).spawn(3) in the order parent, match, other."""
+    ss = np.random.SeedSequence([w.seed, 5]).spawn(3)
+    rp, rm, ro = (np.random.default_rng(s) for s in ss)
+    B, R = w.B, w.R
+    parents = np.full((B, R), -1, dtype=np.int32)
+    for j in range(1, R):
+        if shape == "chain":
+            parents[:, j] = j - 1
+        elif shape == "star":
+            parents[:, j] = 0
+        else:
+            parents[:, j] = rp.integers(max(0, j - width), j, size=B)
+    masks = np.zeros((B, R), dtype=np.uint64)
+    for b in range(B):
+        for i in range(R):
+            m = np.uint64(1) << np.uint64(i)
+            if i > 0:
+                m |= masks[b, parents[b, i]]
+            masks[b, i] = m
+    match = rm.random((B, R)) < p_match
+    other = ro.integers(0, max(w.V - 1, 1), size=(B, R), dtype=np.int64)
+    return TreePlan(w=w, parents=parents, masks=masks, match=match, other=other)
+
+
+def tree_tokens_from_target(plan: TreePlan, target: np.ndarray) -> np.ndarray:
+    """Node j's token is its parent's target token with the planned probability,
+    otherwise another uniformly drawn id; entry 0 (the root) is 0."""
+    t = np.asarray(target, dtype=np.int64)
+    B, R = plan.parents.shape
+    tok = np.zeros((B, R), dtype=np.int32)
+    for j in range(1, R):
+        pt = t[np.arange(B), plan.parents[:, j]]
+        r = plan.other[:, j]
+        tok[:, j] = np.where(plan.match[:, j], pt, r + (r >= pt))
+    return tok
