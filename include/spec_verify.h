@@ -17,6 +17,8 @@
  *   spec_accept        per-row argmax of the target logits, first-mismatch
  *                      prefix against the drafts, acceptance length and the
  *                      committed KV length.
+ *   spec_verify_attn_tree, spec_accept_tree
+ *                      the same two steps for a tree of drafts instead of a chain.
  *   spec_accept_sampled  the same for sampled decoding: lossless stochastic
  *                      acceptance of the drafts and a draw of the next token.
  *   spec_draft_signals confidence and entropy of the draft's distribution and
@@ -152,6 +154,34 @@ sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k
                            const int32_t* block_table, const int32_t* kv_lens, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Tree verification: attention of R = D + 1 draft-tree nodes instead of a chain
+ * of drafts.  The pages' drafter proposes several candidates per position and
+ * the target scores them grouped in one pass (novita.ai blog, section
+ * "Implementation": candidate generation and batch verification); the tree
+ * layout below is this library's.
+ *
+ * Node j of sequence b is new position j: its K and V are at token
+ * L_b - R + j of the cache (node 0 is the last committed token, the root) and
+ * its query is q[b][j].  Node i sees every context key (t < L_b - R) and the
+ * nodes set in tree_mask[b][i]: bit j set iff node j is node i or one of its
+ * ancestors.  Everything else is as for spec_verify_attn (same parameters,
+ * layouts, workspace size and preconditions); a chain tree, mask[i] =
+ * 2^(i+1) - 1, gives spec_verify_attn's result.
+ *
+ *   tree_mask  [B][R] uint64, 8-byte aligned.  Precondition: bit i of
+ *              tree_mask[b][i] is set and no bit above i is set (nodes in
+ *              topological order, parents before children); bits at or above R
+ *              are ignored.
+ * Errors: as spec_verify_attn; SV_ERR_INVALID for a NULL or misaligned
+ * tree_mask; SV_ERR_UNSUPPORTED for batch > 2048.
+ */
+sv_status spec_verify_attn_tree(const sv_attn_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, const int32_t* kv_lens,
+                                const uint64_t* tree_mask, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace spec_accept needs for (batch, draft_len, vocab). */
 sv_status spec_accept_workspace_size(int32_t batch, int32_t draft_len, int32_t vocab,
                                      size_t* bytes);
@@ -184,6 +214,39 @@ sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const flo
                       const int32_t* draft, int32_t* target_tokens, int32_t* accept_len,
                       int32_t* out_tokens, const int32_t* kv_lens_in, int32_t* kv_lens_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy acceptance over a draft tree (the nodes scored by spec_verify_attn_tree).
+ *
+ * For sequence b with R = D + 1 nodes (node 0 = the root, the last committed
+ * token; parents[b][j] < j for j >= 1):
+ *     target_tokens[b][j] = argmax of logits[b][j] (lowest index on ties, as in
+ *                           spec_accept): the target's token after node j
+ *     walk from the root: while the current node i has a child c with
+ *         tokens[b][c] == target_tokens[b][i], step to the lowest such c
+ *     accept_path[b] = the nodes walked, root first, -1 padding
+ *     accept_len[b]  = their number (1 .. 1 + tree depth)
+ *     out_tokens[b]  = tokens of the walked nodes after the root, then the
+ *                      target token of the last one, -1 padding
+ *     kv_lens_out[b] = kv_lens_in[b] - (1 + D) + accept_len[b]
+ * The accepted nodes' K/V rows are at new positions accept_path[b][1..]; the
+ * committed length counts them as positions 1 .. accept_len - 1 after the root,
+ * where the caller moves them (for a chain tree they are already in place).
+ *
+ *   logits      [B][1+D][V] fp32, 16-byte aligned (as spec_accept).
+ *   tokens      [B][1+D] int32: the draft token of each node (entry 0 unused).
+ *   parents     [B][1+D] int32: each node's parent (entry 0 unused); a parent
+ *               outside [0, j) simply never lets node j be walked to.
+ *               tokens and parents may be NULL when draft_len = 0.
+ *   accept_path [B][1+D] int32, written.
+ *   target_tokens, accept_len, out_tokens, kv_lens_in, kv_lens_out and the
+ *   workspace (spec_accept_workspace_size bytes) as for spec_accept.
+ */
+sv_status spec_accept_tree(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
+                           const int32_t* tokens, const int32_t* parents, int32_t* target_tokens,
+                           int32_t* accept_len, int32_t* out_tokens, int32_t* accept_path,
+                           const int32_t* kv_lens_in, int32_t* kv_lens_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace spec_accept_sampled needs for (batch, draft_len, vocab). */
 sv_status spec_accept_sampled_workspace_size(int32_t batch, int32_t draft_len, int32_t vocab,

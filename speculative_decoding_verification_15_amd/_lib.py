@@ -21,6 +21,7 @@ SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1
 EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_workspace_size",
            "spec_accept", "spec_accept_sampled_workspace_size", "spec_accept_sampled",
            "spec_kv_append", "spec_draft_signals_workspace_size", "spec_draft_signals",
+           "spec_verify_attn_tree", "spec_accept_tree",
            "sv_status_string", "sv_last_error", "sv_abi_version")
 
 
@@ -89,6 +90,10 @@ def _load():
     lib.spec_draft_signals.argtypes = [I32, I32, ctypes.c_float, P, P, P, P, I32, ctypes.c_float,
                                        I32, P, S, P]
     lib.spec_draft_signals.restype = U
+    lib.spec_verify_attn_tree.argtypes = [ctypes.POINTER(SvAttnParams)] + [P] * 10 + [S, P]
+    lib.spec_verify_attn_tree.restype = U
+    lib.spec_accept_tree.argtypes = [I32, I32, I32] + [P] * 10 + [S, P]
+    lib.spec_accept_tree.restype = U
     lib.sv_status_string.argtypes = [U]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -230,3 +235,28 @@ def spec_draft_signals(rows, vocab, temperature, draft_logits, confidence, entro
                                    _ptr(confidence), _ptr(entropy), _ptr(next_draft_len),
                                    int(max_draft_len), float(rho), int(group_size),
                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def spec_verify_attn_tree(params: SvAttnParams, q, k_cache, v_cache, k_scale, v_scale,
+                          block_table, kv_lens, tree_mask, out, workspace=None,
+                          workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(_lib.spec_verify_attn_tree(ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                      _ptr(kv_lens), _ptr(tree_mask), _ptr(out), _ptr(workspace),
+                                      workspace_bytes, _stream(stream)))
+
+
+def spec_accept_tree(batch, draft_len, vocab, logits, tokens, parents, target_tokens, accept_len,
+                     out_tokens, accept_path, kv_lens_in, kv_lens_out, workspace,
+                     workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(_lib.spec_accept_tree(batch, draft_len, vocab, _ptr(logits), _ptr(tokens),
+                                 _ptr(parents), _ptr(target_tokens), _ptr(accept_len),
+                                 _ptr(out_tokens), _ptr(accept_path), _ptr(kv_lens_in),
+                                 _ptr(kv_lens_out), _ptr(workspace), workspace_bytes,
+                                 _stream(stream)))

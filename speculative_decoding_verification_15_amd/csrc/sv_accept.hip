@@ -130,6 +130,83 @@ __global__ __launch_bounds__(kWave) void sv_accept_finalize(
   }
 }
 
+// Draft-tree acceptance (nodes in topological order, parent[j] < j, node 0 the
+// root = the last committed token).  grid = B; one wave per sequence; lane j holds tree
+// node j (R <= 64): its row's argmax a_j, its parent and its token.  From the
+// root, the walk steps to the lowest-indexed child c of the current node i with
+// token[c] == a_i (one ballot per step) until no child matches.
+__global__ __launch_bounds__(kWave) void sv_accept_tree_finalize(
+    const ArgmaxPart* __restrict__ part, int chunks, int R, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parents, int32_t* __restrict__ target,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ accept_path, const int32_t* kv_in, int32_t* kv_out) {
+  const int b = blockIdx.x;
+  const int j = threadIdx.x;
+  int a = 0, par = -2, tok = -1;
+  if (j < R) {
+    const ArgmaxPart* p = part + ((size_t)b * R + j) * chunks;
+    float bv = -INFINITY;
+    int bi = INT32_MAX;
+    for (int c = 0; c < chunks; ++c) consider(p[c].value, p[c].index, bv, bi);
+    a = bi;
+    target[(size_t)b * R + j] = a;
+    if (j > 0) {
+      par = parents[(size_t)b * R + j];
+      tok = tokens[(size_t)b * R + j];
+    }
+  }
+  // walk: at most R - 1 steps, the node index grows at each one
+  int cur = 0, len = 1;
+  unsigned long long path = 1ull;           // nodes on the path (node 0, the root)
+  for (int step = 1; step < R; ++step) {
+    const int a_cur = __shfl(a, cur);
+    const unsigned long long m = __ballot(j < R && j > cur && par == cur && tok == a_cur);
+    if (!m) break;
+    cur = __ffsll((long long)m) - 1;
+    path |= 1ull << cur;
+    ++len;
+  }
+  const int a_last = __shfl(a, cur);
+  // Path nodes grow with their place on the path, so a node's place is the
+  // number of path nodes below it.  Every address below is written once.
+  if (j < R) {
+    const bool on_path = (path >> j) & 1ull;
+    const int place = __popcll(path & ((1ull << j) - 1ull));
+    if (on_path) {
+      accept_path[(size_t)b * R + place] = j;
+      if (place > 0) out_tokens[(size_t)b * R + place - 1] = tok;
+    }
+    if (j >= len) {
+      accept_path[(size_t)b * R + j] = -1;
+      out_tokens[(size_t)b * R + j] = -1;
+    }
+    if (j == len - 1) out_tokens[(size_t)b * R + j] = a_last;
+  }
+  if (j == 0) {
+    accept_len[b] = len;
+    kv_out[b] = kv_in[b] - R + len;
+  }
+}
+
+hipError_t launch_accept_tree(int B, int R, int V, const float* logits, const int32_t* tokens,
+                              const int32_t* parents, int32_t* target, int32_t* accept_len,
+                              int32_t* out_tokens, int32_t* accept_path, const int32_t* kv_in,
+                              int32_t* kv_out, void* ws, hipStream_t stream) {
+  const int chunks = argmax_chunks(V);
+  auto* part = static_cast<ArgmaxPart*>(ws);
+  dim3 grid(chunks, B * R);
+  if (V % 4 == 0)
+    sv_argmax_partial<true><<<grid, kArgmaxThreads, 0, stream>>>(logits, V, chunks, part);
+  else
+    sv_argmax_partial<false><<<grid, kArgmaxThreads, 0, stream>>>(logits, V, chunks, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  sv_accept_tree_finalize<<<B, kWave, 0, stream>>>(part, chunks, R, tokens, parents, target,
+                                                    accept_len, out_tokens, accept_path, kv_in,
+                                                    kv_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t* draft,
                          int32_t* target, int32_t* accept_len, int32_t* out_tokens,
                          const int32_t* kv_in, int32_t* kv_out, void* ws, hipStream_t stream) {

@@ -101,10 +101,11 @@ sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes
   return SV_OK;
 }
 
-sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k_cache,
-                           const void* v_cache, const float* k_scale, const float* v_scale,
-                           const int32_t* block_table, const int32_t* kv_lens, void* out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+static sv_status run_attn(const sv_attn_params* p, const void* q, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* kv_lens,
+                          const uint64_t* tree_mask, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   sv::AttnPlan plan;
   sv_status s = make_attn_plan(p, plan);
   if (s != SV_OK) return s;
@@ -121,6 +122,11 @@ sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k
   } else if (k_scale || v_scale) {
     return fail(SV_ERR_INVALID, "k_scale and v_scale must be NULL for bf16 caches");
   }
+  if (tree_mask && !aligned(tree_mask, 8))
+    return fail(SV_ERR_INVALID, "tree_mask must be 8-byte aligned");
+  if (tree_mask && !plan.streamk)
+    return fail(SV_ERR_UNSUPPORTED, "tree verification needs batch <= %d (got %d)",
+                sv::kStreamMaxBatch, p->batch);
   if (plan.ws_bytes > 0) {
     if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
     if (workspace_bytes < plan.ws_bytes)
@@ -128,11 +134,30 @@ sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k
                   plan.ws_bytes);
     if (!aligned(workspace, 256)) return fail(SV_ERR_INVALID, "workspace must be 256-byte aligned");
   }
-  sv::AttnPtrs ptrs{q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, out, workspace};
+  sv::AttnPtrs ptrs{q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, out, workspace,
+                    tree_mask};
   hipError_t e = sv::launch_attention(plan, ptrs, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return SV_OK;
+}
+
+sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k_cache,
+                           const void* v_cache, const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* kv_lens, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attn(p, q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, nullptr, out,
+                  workspace, workspace_bytes, stream);
+}
+
+sv_status spec_verify_attn_tree(const sv_attn_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, const int32_t* kv_lens,
+                                const uint64_t* tree_mask, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!tree_mask) return fail(SV_ERR_INVALID, "tree_mask is NULL");
+  return run_attn(p, q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, tree_mask, out,
+                  workspace, workspace_bytes, stream);
 }
 
 static sv_status check_accept_shape(int32_t batch, int32_t draft_len, int32_t vocab) {
@@ -176,6 +201,37 @@ sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const flo
   hipError_t e = sv::launch_accept(batch, draft_len, vocab, logits, draft, target_tokens,
                                    accept_len, out_tokens, kv_lens_in, kv_lens_out, workspace,
                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+sv_status spec_accept_tree(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
+                           const int32_t* tokens, const int32_t* parents, int32_t* target_tokens,
+                           int32_t* accept_len, int32_t* out_tokens, int32_t* accept_path,
+                           const int32_t* kv_lens_in, int32_t* kv_lens_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  sv_status s = check_accept_shape(batch, draft_len, vocab);
+  if (s != SV_OK) return s;
+  if (!logits || !target_tokens || !accept_len || !out_tokens || !accept_path || !kv_lens_in ||
+      !kv_lens_out)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (draft_len > 0 && (!tokens || !parents))
+    return fail(SV_ERR_INVALID, "tokens and parents are required with draft_len > 0");
+  if (!aligned(logits, 16)) return fail(SV_ERR_INVALID, "logits must be 16-byte aligned");
+  if (!aligned(target_tokens, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
+      !aligned(accept_path, 4) || !aligned(kv_lens_in, 4) || !aligned(kv_lens_out, 4) ||
+      (tokens && !aligned(tokens, 4)) || (parents && !aligned(parents, 4)))
+    return fail(SV_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  const size_t need = sv::accept_workspace_bytes(batch, draft_len, vocab);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(SV_ERR_INVALID, "workspace must be 256-byte aligned");
+  hipError_t e = sv::launch_accept_tree(batch, draft_len + 1, vocab, logits, tokens, parents,
+                                        target_tokens, accept_len, out_tokens, accept_path,
+                                        kv_lens_in, kv_lens_out, workspace,
+                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return SV_OK;

@@ -60,12 +60,25 @@ struct AttnArgs {
   float* ws_f;    // stream-K: power-of-two factor f of each slot row
   int B, R, H_q, H_kv, G, M;
   int max_blocks, num_blocks, max_kv_len;
-  int split_tokens, s_max, m_tiles;
+  int split_tokens;
+  union {
+    int s_max;         // split path: splits per sequence
+    uint32_t tree_lo;  // stream-K tree variants: low word of the ancestor-mask pointer
+  };
+  int m_tiles;
   int min_tiles;  // stream-K: least tiles per workgroup
   float c;        // sm_scale * log2(e)
   int* sk_meta;   // stream-K: [W, Wp, pref[0..B]] written by workgroup 0 for the merge
   int sk_rows;    // stream-K: rows per unit (128 or 256)
+  uint32_t tree_hi;  // stream-K tree variants: high word of the ancestor-mask pointer
+                     // (the struct's trailing padding, so the layout is unchanged)
 };
+
+// Tree variants: [B][R] ancestor masks, bit j of mask[b][i] = node j is node i
+// or one of its ancestors.
+__device__ __forceinline__ const uint64_t* tree_masks(const AttnArgs& a) {
+  return reinterpret_cast<const uint64_t*>(((uint64_t)a.tree_hi << 32) | a.tree_lo);
+}
 
 // Row i of the 32-key score block holds key pi(i) of that block.
 __device__ __forceinline__ int key_of_row(int i) {
@@ -870,7 +883,6 @@ void sv_attn_partial_ring(AttnArgs a) {
 // flight.  (A fifth stage, which LDS would allow now that the prefix table
 // lives in the ring, measured no faster.)
 // ---------------------------------------------------------------------------
-constexpr int kStreamMaxBatch = 2048;
 constexpr int kStreamRows = 128;          // rows per unit of 4 waves x 32 (8-wave units: 256)
 constexpr int kSkKeys = 32;               // keys per stream-K tile
 
@@ -1022,6 +1034,26 @@ __device__ __forceinline__ void sk_mask(f32x16& x, const RowCtx& r, int kt) {
   }
 }
 
+// Tree verification: new position j (key P + j) holds draft-tree node j, and
+// node i sees the context and the nodes set in its ancestor mask (itself and
+// its ancestors).  The mask is read here, on the tiles that reach past P only;
+// the load's wait is the compiler's own, which only adds to the ring's waits.
+__device__ __forceinline__ void sk_mask_tree(f32x16& x, const RowCtx& r, int kt, const AttnArgs& a) {
+  const uint64_t live = a.R == 64 ? ~0ull : ((1ull << a.R) - 1);
+  const uint64_t anc = tree_masks(a)[(size_t)r.b * a.R + r.pos] & live;
+  // The shift amount is clamped into [0, 63] before the shift: the selects
+  // below evaluate the shift for every key, and an out-of-range amount (a
+  // context key, j < 0) must not reach it.
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int j = kt + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3)) - r.P;
+    const uint32_t sh = (uint32_t)min(max(j, 0), 63);
+    const bool in_tree = ((anc >> sh) & 1ull) != 0;
+    const bool hidden = j >= 0 && (j >= a.R || !in_tree);
+    x[v] = hidden ? -INFINITY : x[v];
+  }
+}
+
 // V operands of one tile (V past the end of the sequence already zeroed).
 template <int HD>
 __device__ __forceinline__ void sk_read_v(const uint8_t* stage, int v_lds,
@@ -1099,7 +1131,8 @@ __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
 // read by that unit alone (one row tile per KV head).  WAVES = 4 (units of 128
 // rows, two workgroups per CU) or 8 (units of 256 rows, one per CU), so that
 // up to 256 rows of one KV head stream its K and V once.
-template <int HD, int NS, int WPE, bool NT, int WAVES>
+// TREE: draft-tree verification (ancestor masks instead of the causal chain).
+template <int HD, int NS, int WPE, bool NT, int WAVES, bool TREE>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void sv_attn_streamk(AttnArgs a) {
@@ -1258,7 +1291,10 @@ void sv_attn_streamk(AttnArgs a) {
       // computed (MFMA) while the softmax of tile g runs (VALU); they are kept
       // when tile g + 1 continues this segment, which has the same Q.
       f32x16 x = have_xn ? xn : sk_scores<HD>(stage, k_lds, qop);
-      if (kt + kSkKeys - 1 > r.P) sk_mask(x, r, kt);   // unless every key is visible to every row
+      if (kt + kSkKeys - 1 > r.P) {            // unless every key is visible to every row
+        if constexpr (TREE) sk_mask_tree(x, r, kt, a);
+        else sk_mask(x, r, kt);
+      }
       xn = sk_scores<HD>(smem + ((t + 1) % NS) * STAGE, k_lds, qop);
       bf16x8 vop[2][DB];
       sk_read_v<HD>(stage, v_lds, vop);
@@ -1310,7 +1346,7 @@ struct SkTile8 {
   static constexpr int kStages = 3;
 };
 
-template <int HD, int WPE, bool NT>
+template <int HD, int WPE, bool NT, bool TREE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void sv_attn_streamk_fp8(AttnArgs a) {
@@ -1526,7 +1562,10 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     }
     if (active) {
       f32x16 x = have_xn ? xn : sk_scores<HD>(im, k_lds, qop);
-      if (kt + kSkKeys - 1 > r.P) sk_mask(x, r, kt);   // unless every key is visible to every row
+      if (kt + kSkKeys - 1 > r.P) {            // unless every key is visible to every row
+        if constexpr (TREE) sk_mask_tree(x, r, kt, a);
+        else sk_mask(x, r, kt);
+      }
       xn = sk_scores<HD>(img + i1 * STAGE, k_lds, qop);
       const f32x4 mt4 = s_mant[i0];
       float alpha;
@@ -1880,22 +1919,23 @@ void plan_attention(AttnPlan& p, int split_request) {
   p.ws_bytes = p.ws_ml_offset + rows * sizeof(f32x2);
 }
 
-template <int HD>
+template <int HD, bool TREE>
 static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
   // Row tiles of one KV head share its K/V through L2; a lone row tile reads
   // them once, so they stream past the caches.
+  constexpr int S4 = SkTile<HD>::kStages, S8 = SkTile<HD>::kStages8;
   if (p.fp8 && p.m_tiles == 1)
-    sv_attn_streamk_fp8<HD, kStreamWPE, true><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk_fp8<HD, kStreamWPE, true, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.fp8)
-    sv_attn_streamk_fp8<HD, kStreamWPE, false><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk_fp8<HD, kStreamWPE, false, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.waves == 8 && p.m_tiles == 1)
-    sv_attn_streamk<HD, SkTile<HD>::kStages8, 2, true, 8><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
+    sv_attn_streamk<HD, S8, 2, true, 8, TREE><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
   else if (p.waves == 8)
-    sv_attn_streamk<HD, SkTile<HD>::kStages8, 2, false, 8><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
+    sv_attn_streamk<HD, S8, 2, false, 8, TREE><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
   else if (p.m_tiles == 1)
-    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, true, 4><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk<HD, S4, kStreamWPE, true, 4, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else
-    sv_attn_streamk<HD, SkTile<HD>::kStages, kStreamWPE, false, 4><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk<HD, S4, kStreamWPE, false, 4, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = p.B * p.H_kv * p.m_tiles;
@@ -1971,7 +2011,16 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   a.s_max = p.s_max;
   a.m_tiles = p.m_tiles;
   a.c = p.sm_scale * kLog2e;
-  if (p.streamk) return p.hd == 128 ? launch_streamk<128>(p, a, stream) : launch_streamk<64>(p, a, stream);
+  a.tree_hi = 0;
+  if (ptr.tree_mask) {
+    if (!p.streamk) return hipErrorInvalidValue;   // the host rejects trees off the stream-K path
+    const uint64_t tm = reinterpret_cast<uint64_t>(ptr.tree_mask);
+    a.tree_lo = (uint32_t)tm;
+    a.tree_hi = (uint32_t)(tm >> 32);
+    return p.hd == 128 ? launch_streamk<128, true>(p, a, stream) : launch_streamk<64, true>(p, a, stream);
+  }
+  if (p.streamk)
+    return p.hd == 128 ? launch_streamk<128, false>(p, a, stream) : launch_streamk<64, false>(p, a, stream);
   if (p.hd == 128)
     return p.fp8 ? launch_typed<128, true>(p, a, stream) : launch_typed<128, false>(p, a, stream);
   return p.fp8 ? launch_typed<64, true>(p, a, stream) : launch_typed<64, false>(p, a, stream);

@@ -10,6 +10,8 @@ namespace sv {
 
 // Keys per attention tile iteration; split boundaries are multiples of it.
 constexpr int kAttnTile = 64;
+// Batches up to this size take the stream-K path (its prefix table lives in LDS).
+constexpr int kStreamMaxBatch = 2048;
 // Query rows per wave (one 32-wide MFMA operand).
 constexpr int kRowsPerWave = 32;
 
@@ -42,6 +44,7 @@ struct AttnPtrs {
   const int32_t* kv_lens;
   void* out;
   void* ws;
+  const uint64_t* tree_mask;  // NULL: causal chain; else [B][R] ancestor masks
 };
 
 // Fills split/grid/workspace fields of `plan` from its shape fields.

@@ -24,6 +24,12 @@ hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t
                          int32_t* target, int32_t* accept_len, int32_t* out_tokens,
                          const int32_t* kv_in, int32_t* kv_out, void* ws, hipStream_t stream);
 
+// Draft-tree acceptance: same argmax workspace as greedy acceptance (R = 1 + D rows).
+hipError_t launch_accept_tree(int B, int R, int V, const float* logits, const int32_t* tokens,
+                              const int32_t* parents, int32_t* target, int32_t* accept_len,
+                              int32_t* out_tokens, int32_t* accept_path, const int32_t* kv_in,
+                              int32_t* kv_out, void* ws, hipStream_t stream);
+
 // Stochastic acceptance: one (max, fp64 sum) record of 16 bytes per 4096-logit
 // chunk of every target row (B (1 + D)) and draft row (B D); a 32-byte draw
 // record per sequence; two fp64 weight sums per chunk of each sequence's drawn row.

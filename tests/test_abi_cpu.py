@@ -389,3 +389,42 @@ def test_draft_signals_errors(kw, status):
 @pytest.mark.parametrize("rows,V", [(1, 1), (32, 128256), (7, 4097), (65535, 10)])
 def test_draft_signals_workspace_size(rows, V):
     assert sv.spec_draft_signals_workspace_size(rows, V) == rows * (-(-V // 4096)) * 32
+
+
+def test_attn_tree_errors():
+    lib = sv.library()
+    p = good_params()
+
+    def call(tm, **kw):
+        pp = good_params(**kw)
+        return lib.spec_verify_attn_tree(ctypes.byref(pp), FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                         tm, FAKE * 2, FAKE * 4, 1 << 40, None)
+    assert call(None) == sv.SV_ERR_INVALID
+    assert call(FAKE + 4) == sv.SV_ERR_INVALID
+    assert call(FAKE, batch=3000) == sv.SV_ERR_UNSUPPORTED        # split-K path: no trees
+    assert call(FAKE, draft_len=64) == sv.SV_ERR_INVALID
+    assert p.batch == 4
+
+
+def call_accept_tree(B=4, D=3, V=1000, ws_bytes=1 << 40, **ptrs):
+    a = dict(lg=FAKE, tok=FAKE, par=FAKE, tgt=FAKE, al=FAKE, out=FAKE, path=FAKE, kvi=FAKE,
+             kvo=FAKE, ws=FAKE * 4)
+    a.update(ptrs)
+    return sv.library().spec_accept_tree(B, D, V, a["lg"], a["tok"], a["par"], a["tgt"], a["al"],
+                                         a["out"], a["path"], a["kvi"], a["kvo"], a["ws"],
+                                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID), (dict(D=64), sv.SV_ERR_INVALID), (dict(V=0), sv.SV_ERR_INVALID),
+    (dict(lg=None), sv.SV_ERR_INVALID), (dict(tok=None), sv.SV_ERR_INVALID),
+    (dict(par=None), sv.SV_ERR_INVALID), (dict(path=None), sv.SV_ERR_INVALID),
+    (dict(lg=FAKE + 4), sv.SV_ERR_INVALID), (dict(par=FAKE + 2), sv.SV_ERR_INVALID),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE), (dict(ws_bytes=4 * 4 * 8 - 1), sv.SV_ERR_WORKSPACE),
+])
+def test_accept_tree_errors(kw, status):
+    assert call_accept_tree(**kw) == status
+
+
+def test_accept_tree_no_drafts_allows_null_tree():
+    assert call_accept_tree(D=0, tok=None, par=None, ws=None) == sv.SV_ERR_WORKSPACE
