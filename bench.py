@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+LEG_WARMUP = 30          # untimed calls before each side measurement
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "verified tokens/sec + KV HBM GB/s (% peak) at Llama-70B-like GQA, D=15"
 KERNEL_SOURCES = ("speculative_decoding_verification_15_amd/csrc/sv_attn.hip",
@@ -114,7 +115,8 @@ def time_append(w, da, stream, sv, calls=20):
                                 num_blocks=da.inp.num_blocks,
                                 kv_dtype=sv.SV_KV_FP8_E4M3 if fp8 else sv.SV_KV_BF16)
     sh = stream.cuda_stream
-    sv.spec_kv_append(prm, kn, vn, da.k, da.v, da.ks, da.vs, da.bt, kin, kout, stream=sh)
+    for _ in range(LEG_WARMUP):        # the GPU idled during input generation: clocks ramp up
+        sv.spec_kv_append(prm, kn, vn, da.k, da.v, da.ks, da.vs, da.bt, kin, kout, stream=sh)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(calls):
@@ -150,7 +152,8 @@ def time_accept_sampled(w, da, stream, sv, calls=20):
     def call():
         sv.spec_accept_sampled(B, D, V, si.tau, zt, zd, dr, ua, us, al, out, da.kl, kout, ws,
                                ws_bytes, stream=sh)
-    call()
+    for _ in range(LEG_WARMUP):        # the GPU idled during input generation: clocks ramp up
+        call()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(calls):
@@ -183,7 +186,8 @@ def time_draft_signals(w, stream, sv, calls=20):
     def call():
         sv.spec_draft_signals(w.B, w.V, 1.0, z, conf, ent, nd, w.D, 0.05, w.G, ws, ws_bytes,
                               stream=sh)
-    call()
+    for _ in range(LEG_WARMUP):        # the GPU idled during input generation: clocks ramp up
+        call()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(calls):
@@ -195,6 +199,55 @@ def time_draft_signals(w, stream, sv, calls=20):
     return {"kernels": "sv_draft_stats + sv_draft_decide", "avg_launch_us": round(us_call, 2),
             "algorithmic_bytes": moved, "GBps": round(moved / (us_call * 1e-6) / 1e9, 1),
             "next_draft_len_hist": np.bincount(nd.cpu().numpy(), minlength=w.D + 1).tolist()}
+
+
+def time_tree(w, da, p, ws, ws_bytes, out, stream, sv, calls=20):
+    """Tree verification on the workload's shape: spec_verify_attn_tree with a
+    random draft tree of 1 + D nodes per sequence (each node's parent among the 3
+    nodes before it), then spec_accept_tree on the first logit set, timed with
+    HIP events after the step's own timing."""
+    import torch
+    from tests.gpu_util import dev
+    from workloads import make_accept_plan, make_tree_plan, tree_tokens_from_target
+    tp = make_tree_plan(w, shape="random", width=3, p_match=0.7)
+    tm = torch.from_numpy(np.ascontiguousarray(tp.masks).view(np.int64)).cuda()
+    plan = make_accept_plan(w)
+    tok = dev(tree_tokens_from_target(tp, np.argmax(plan.logits, axis=-1)))
+    par = dev(tp.parents)
+    lg = dev(plan.logits)
+    B, D, V, R = w.B, w.D, w.V, w.R
+    tgt = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    otok = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    kout = torch.empty((B,), dtype=torch.int32, device="cuda")
+    acc_ws_bytes = sv.spec_accept_workspace_size(B, D, V)
+    acc_ws = torch.empty(acc_ws_bytes, dtype=torch.uint8, device="cuda")
+    sh = stream.cuda_stream
+
+    def attn():
+        sv.spec_verify_attn_tree(p, da.q, da.k, da.v, da.ks, da.vs, da.bt, da.kl, tm, out, ws,
+                                 ws_bytes, stream=sh)
+
+    def acc():
+        sv.spec_accept_tree(B, D, V, lg, tok, par, tgt, al, otok, path, da.kl, kout, acc_ws,
+                            acc_ws_bytes, stream=sh)
+    res = {}
+    for name, fn in (("attn", attn), ("accept", acc)):
+        for _ in range(LEG_WARMUP):    # the GPU idled during input generation: clocks ramp up
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(calls):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = ev[0].elapsed_time(ev[1]) * 1e3 / calls
+    return {"kernels": "sv_attn_streamk (tree variant) + merge; sv_argmax_partial + "
+                       "sv_accept_tree_finalize",
+            "attn_avg_launch_us": round(res["attn"], 2),
+            "accept_avg_launch_us": round(res["accept"], 2),
+            "sum_accept_len": int(al.cpu().sum())}
 
 
 def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
@@ -226,8 +279,8 @@ def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama31_70b_gqa8_d15")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -328,6 +381,7 @@ def main():
     append = time_append(w, da, stream, sv)
     sampled = time_accept_sampled(w, da, stream, sv)
     signals = time_draft_signals(w, stream, sv)
+    tree = time_tree(w, da, p, ws, ws_bytes, out, stream, sv) if w.B <= 2048 else None
 
     ms_per_step = total_ms / args.steps
     value = tokens_timed / (total_ms / 1e3)
@@ -379,6 +433,7 @@ def main():
         "append": append,
         "accept_sampled": sampled,
         "draft_signals": signals,
+        "tree": tree,
         "sum_accept_len_per_step": round(tokens_timed / args.steps, 2),
         "kernel_src_sha": src_hash,
         "input_gen_s": round(t_gen, 1),
