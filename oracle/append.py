@@ -87,12 +87,18 @@ def _block_scale(amax: np.float32) -> np.float32:
 
 
 def oracle_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens,
-                     fp8: bool):
+                     fp8: bool, accept_path=None):
     """Append the R new K/V rows of every sequence; returns new arrays
     (k_cache, v_cache, k_scale, v_scale, kv_lens_out).  Inputs are not modified.
 
     k_new, v_new  [B][R][H_kv][hd] uint16 bf16 bits
     kv_lens       [B] committed lengths before the append (c_b)
+
+    With ``accept_path`` ([B][R], a tree acceptance's walked nodes, root first,
+    -1 padded): the tree commit.  kv_lens are then the committed lengths after
+    the acceptance; the rows of the accepted nodes after the root, in path
+    order, are appended by the same rule at kv_lens[b] - (AL - 1), right behind
+    the root, and the lengths are returned unchanged (reading T4).
     """
     k_new = np.asarray(k_new, dtype=np.uint16)
     v_new = np.asarray(v_new, dtype=np.uint16)
@@ -115,27 +121,30 @@ def oracle_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tab
         t = np.asarray(slots)[:, None]
         return (blk, h, d[None, :], t)
 
-    for b in range(B):
-        c = int(lens[b])
+    def append_seq(b, krows, vrows, c):
+        """Rows krows/vrows [n][H_kv][hd] (bf16 bits) of sequence b at positions c .. c+n-1."""
+        n = krows.shape[0]
+        if n == 0:
+            return
         if not fp8:
-            for i in range(R):
+            for i in range(n):
                 pos = c + i
                 blk = int(block_table[b][pos // BLOCK])
                 slot = pos % BLOCK
                 for h in range(H_kv):
-                    kc[k_at(blk, h, [slot])] = k_new[b, i, h, :][None, :]
-                    vc[v_at(blk, h, [slot])] = v_new[b, i, h, :][None, :]
-            continue
+                    kc[k_at(blk, h, [slot])] = krows[i, h, :][None, :]
+                    vc[v_at(blk, h, [slot])] = vrows[i, h, :][None, :]
+            return
         # e4m3: per touched block and KV head, for K and V independently
-        first_blk, last_blk = c // BLOCK, (c + R - 1) // BLOCK
+        first_blk, last_blk = c // BLOCK, (c + n - 1) // BLOCK
         for j in range(first_blk, last_blk + 1):
             blk = int(block_table[b][j])
             start = j * BLOCK
             a = max(c - start, 0)                       # held slots 0 .. a-1
-            lo, hi = max(c, start), min(c + R, start + BLOCK)
+            lo, hi = max(c, start), min(c + n, start + BLOCK)
             for h in range(H_kv):
-                for new, cache, scale, at in ((k_new, kc, ks, k_at), (v_new, vc, vs, v_at)):
-                    x = bf16_bits_to_f64(new[b, lo - c: hi - c, h, :]).astype(np.float32)
+                for rows, cache, scale, at in ((krows, kc, ks, k_at), (vrows, vc, vs, v_at)):
+                    x = bf16_bits_to_f64(rows[lo - c: hi - c, h, :]).astype(np.float32)
                     amax_new = np.float32(np.abs(x).max()) if x.size else np.float32(0)
                     if a == 0:
                         s = _block_scale(amax_new)
@@ -155,4 +164,18 @@ def oracle_kv_append(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tab
                     cache[at(blk, h, range(lo - start, hi - start))] = \
                         e4m3_encode_f32((x / s).astype(np.float32))
                     scale[blk, h] = s
-    return kc, vc, ks, vs, (lens + R).astype(np.int32)
+
+    if accept_path is None:
+        for b in range(B):
+            append_seq(b, k_new[b], v_new[b], int(lens[b]))
+        return kc, vc, ks, vs, (lens + R).astype(np.int32)
+    # tree commit: the accepted nodes after the root, right behind it
+    path = np.asarray(accept_path, dtype=np.int64)
+    for b in range(B):
+        nodes = []
+        for x in path[b, 1:]:
+            if x < 0:
+                break
+            nodes.append(int(x))
+        append_seq(b, k_new[b, nodes], v_new[b, nodes], int(lens[b]) - len(nodes))
+    return kc, vc, ks, vs, lens.astype(np.int32)

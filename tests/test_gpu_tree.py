@@ -67,6 +67,18 @@ def test_tree_attention_all_elements(name, shape):
     _check(gpu, _oracle(inp, plan.parents), f"{name}/{shape}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_tree_attention_256_row_units(kv):
+    """G (1 + D) = 192 rows per KV head: one 8-wave, 256-row unit per KV head
+    (bf16), or two 128-row tiles (e4m3)."""
+    w = MINI["mini_gqa8_d15"].replace(name=f"tree_g8_d23_{kv}", D=23, kv_dtype=kv,
+                                       T_range=(100, 1500))
+    inp = make_attn_inputs(w)
+    plan = make_tree_plan(w, shape="random", width=4)
+    gpu = DeviceAttn.to_f64(run_tree_attention(inp, plan.masks)[0])
+    _check(gpu, _oracle(inp, plan.parents), w.name)
+
+
 def test_tree_attention_64_nodes():
     w = EDGE["edge_d63"]
     inp = make_attn_inputs(w)

@@ -287,3 +287,89 @@ def test_rollback_by_length_then_append_overwrites_rejected_rows():
         np.testing.assert_array_equal(V[c: c + al], bf16_bits_to_f64(v1[b, :al]))
         np.testing.assert_array_equal(K[c + al:], bf16_bits_to_f64(k2[b]))
         np.testing.assert_array_equal(V[c + al:], bf16_bits_to_f64(v2[b]))
+
+
+def _tree_step(fp8, seed=21):
+    """An append of a random tree's 16 node rows after ragged contexts, then the
+    greedy tree acceptance of the oracle: returns everything the commit needs."""
+    from oracle.accept import oracle_argmax
+    from oracle.tree import oracle_accept_tree
+    from workloads import make_tree_plan, tree_tokens_from_target
+    w = MINI["mini_gqa8_d15"].replace(B=3, V=30)
+    B, R, H, hd = w.B, w.R, 2, 64
+    rng = np.random.default_rng(seed)
+    kc, vc, ks, vs, table = _empty_cache(B, H, hd, fp8, 160, seed=seed)
+    # held context: one whole block each, then lengths 16, 5, 13 (valid codes)
+    ctx = [_rows(rng, (B, 16, H, hd)) for _ in range(2)]
+    kc, vc, ks, vs, _ = oracle_kv_append(*ctx, kc, vc, ks, vs, table, np.zeros(B, np.int32), fp8)
+    T = np.array([16, 5, 13], np.int32)
+    k_new, v_new = _rows(rng, (B, R, H, hd), 2.0), _rows(rng, (B, R, H, hd), 2.0)
+    kc, vc, ks, vs, L = oracle_kv_append(k_new, v_new, kc, vc, ks, vs, table, T, fp8)
+    logits = rng.standard_normal((B, R, w.V)).astype(np.float32)
+    tp = make_tree_plan(w, shape="random", width=3, p_match=0.9)
+    tok = tree_tokens_from_target(tp, oracle_argmax(logits))
+    acc = oracle_accept_tree(logits, tok, tp.parents, L)
+    return dict(k_new=k_new, v_new=v_new, kc=kc, vc=vc, ks=ks, vs=vs, table=table, T=T, acc=acc)
+
+
+def test_tree_commit_moves_accepted_rows_behind_the_root_bf16():
+    st = _tree_step(False)
+    acc = st["acc"]
+    assert acc["accept_len"].max() > 2
+    kc, vc, _, _, lens = oracle_kv_append(st["k_new"], st["v_new"], st["kc"], st["vc"], None,
+                                          None, st["table"], acc["kv_lens_out"], False,
+                                          accept_path=acc["accept_path"])
+    np.testing.assert_array_equal(lens, acc["kv_lens_out"])
+    for b in range(3):
+        AL, T = int(acc["accept_len"][b]), int(st["T"][b])
+        assert lens[b] == T + AL
+        path = acc["accept_path"][b, :AL]
+        K, V = gather_kv(kc, vc, None, None, st["table"], b, int(lens[b]))
+        np.testing.assert_array_equal(K[T:], bf16_bits_to_f64(st["k_new"][b, path]))
+        np.testing.assert_array_equal(V[T:], bf16_bits_to_f64(st["v_new"][b, path]))
+        K0, _ = gather_kv(st["kc"], st["vc"], None, None, st["table"], b, T)
+        np.testing.assert_array_equal(K[:T], K0)
+
+
+def test_tree_commit_of_a_chain_leaves_a_bf16_cache_unchanged():
+    st = _tree_step(False)
+    AL = np.array([16, 3, 1], np.int32)
+    path = np.full((3, 16), -1, np.int32)
+    for b in range(3):
+        path[b, :AL[b]] = np.arange(AL[b])
+    kv = st["T"] + AL
+    kc, vc, _, _, lens = oracle_kv_append(st["k_new"], st["v_new"], st["kc"], st["vc"], None,
+                                          None, st["table"], kv, False, accept_path=path)
+    np.testing.assert_array_equal(kc, st["kc"])
+    np.testing.assert_array_equal(vc, st["vc"])
+    np.testing.assert_array_equal(lens, kv)
+
+
+def test_tree_commit_e4m3_rounding_and_amax_rule():
+    st = _tree_step(True)
+    acc = st["acc"]
+    kc, vc, ks, vs, lens = oracle_kv_append(st["k_new"], st["v_new"], st["kc"], st["vc"],
+                                            st["ks"], st["vs"], st["table"], acc["kv_lens_out"],
+                                            True, accept_path=acc["accept_path"])
+    for b in range(3):
+        AL, T = int(acc["accept_len"][b]), int(st["T"][b])
+        for k, node in enumerate(acc["accept_path"][b, 1:AL], start=1):
+            pos = T + k
+            blk, slot = st["table"][b][pos // BLOCK], pos % BLOCK
+            for cache, scale, rows in ((kc, ks, st["k_new"]), (vc, vs, st["v_new"])):
+                for h in range(2):
+                    dec, _ = _decoded_block(cache, scale, blk, h, slice(slot, slot + 1))
+                    x = bf16_bits_to_f64(rows[b, node, h])
+                    y = (x.astype(np.float32) / scale[blk, h]).astype(np.float64)
+                    assert (np.abs(dec[0] / scale[blk, h] - y) <= _half_step(y)).all()
+        # a block whose scale the commit recomputed holds 448 as its largest code;
+        # one that kept its scale may not (a rejected row may have set it)
+        for j in range((T + 1) // BLOCK, (T + AL - 1) // BLOCK + 1) if AL > 1 else []:
+            n = min(BLOCK, int(lens[b]) - j * BLOCK)
+            blk = st["table"][b][j]
+            for h in range(2):
+                for cache, scale, before in ((kc, ks, st["ks"]), (vc, vs, st["vs"])):
+                    if scale[blk, h] == before[blk, h]:
+                        continue
+                    _, codes = _decoded_block(cache, scale, blk, h, slice(0, n))
+                    assert (codes & 0x7F).max() == 0x7E
