@@ -17,8 +17,9 @@
  *   spec_accept        per-row argmax of the target logits, first-mismatch
  *                      prefix against the drafts, acceptance length and the
  *                      committed KV length.
- *   spec_verify_attn_tree, spec_accept_tree
- *                      the same two steps for a tree of drafts instead of a chain.
+ *   spec_verify_attn_tree, spec_accept_tree, spec_kv_commit_tree
+ *                      the same steps for a tree of drafts instead of a chain, and
+ *                      the move of the accepted nodes' K/V behind the root.
  *   spec_accept_sampled  the same for sampled decoding: lossless stochastic
  *                      acceptance of the drafts and a draw of the next token.
  *   spec_draft_signals confidence and entropy of the draft's distribution and
@@ -354,6 +355,29 @@ sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const voi
                          void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                          const int32_t* block_table, const int32_t* kv_lens_in,
                          int32_t* kv_lens_out, void* stream);
+
+/*
+ * Tree commit: the KV step after spec_accept_tree.  With kv_lens[b] already
+ * committed to L_b - R + AL (spec_accept_tree's kv_lens_out), the rows of the
+ * accepted nodes after the root, k_new/v_new[b][accept_path[b][k]] for k = 1 ..
+ * AL - 1, are appended right behind the root, at token positions kv_lens[b] -
+ * (AL - 1) + (k - 1), by spec_kv_append's rule (e4m3 scales included); AL is
+ * the number of entries of accept_path[b] before its first -1.  kv_lens is not
+ * written.  For a chain tree the rows are rewritten in place.  Tree layout:
+ * see spec_verify_attn_tree.
+ *
+ *   p            as for spec_kv_append, num_new = R = 1 + D (<= 64) nodes.
+ *   k_new, v_new [B][R][H_kv][hd] bf16: the step's node rows (those given to
+ *                spec_kv_append before the attention).
+ *   accept_path  [B][R] int32 from spec_accept_tree, 4-byte aligned.
+ *   kv_lens      [B] int32, the committed lengths; read only.
+ *   caches, scales, block_table: as for spec_kv_append.
+ * Errors: as spec_kv_append; SV_ERR_INVALID for a NULL accept_path or R > 64.
+ */
+sv_status spec_kv_commit_tree(const sv_append_params* p, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* block_table, const int32_t* accept_path,
+                              const int32_t* kv_lens, void* stream);
 
 /* Bytes of device workspace spec_draft_signals needs for (rows, vocab). */
 sv_status spec_draft_signals_workspace_size(int32_t rows, int32_t vocab, size_t* bytes);

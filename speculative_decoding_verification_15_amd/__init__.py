@@ -9,6 +9,7 @@ from ._lib import (EXPORTS, LIB_PATH, SV_ERR_INVALID, SV_ERR_LAUNCH, SV_ERR_UNSU
                    SvAttnParams, SvError, abi_version, last_error, library, make_append_params,
                    make_attn_params, spec_accept, spec_kv_append, spec_draft_signals,
                    spec_draft_signals_workspace_size, spec_verify_attn_tree, spec_accept_tree,
+                   spec_kv_commit_tree,
                    spec_accept_sampled, spec_accept_sampled_workspace_size,
                    spec_accept_workspace_size, spec_verify_attn, spec_verify_attn_workspace_size,
                    status_string)
@@ -19,6 +20,7 @@ __all__ = [
     "abi_version", "last_error", "library", "make_append_params", "make_attn_params",
     "spec_accept", "spec_accept_sampled", "spec_kv_append", "spec_draft_signals",
     "spec_draft_signals_workspace_size", "spec_verify_attn_tree", "spec_accept_tree",
+    "spec_kv_commit_tree",
     "spec_accept_sampled_workspace_size", "spec_accept_workspace_size",
     "spec_verify_attn", "spec_verify_attn_workspace_size", "status_string",
 ]

@@ -21,7 +21,7 @@ SV_KV_BF16, SV_KV_FP8_E4M3 = 0, 1
 EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_workspace_size",
            "spec_accept", "spec_accept_sampled_workspace_size", "spec_accept_sampled",
            "spec_kv_append", "spec_draft_signals_workspace_size", "spec_draft_signals",
-           "spec_verify_attn_tree", "spec_accept_tree",
+           "spec_verify_attn_tree", "spec_accept_tree", "spec_kv_commit_tree",
            "sv_status_string", "sv_last_error", "sv_abi_version")
 
 
@@ -94,6 +94,8 @@ def _load():
     lib.spec_verify_attn_tree.restype = U
     lib.spec_accept_tree.argtypes = [I32, I32, I32] + [P] * 10 + [S, P]
     lib.spec_accept_tree.restype = U
+    lib.spec_kv_commit_tree.argtypes = [ctypes.POINTER(SvAppendParams)] + [P] * 10
+    lib.spec_kv_commit_tree.restype = U
     lib.sv_status_string.argtypes = [U]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -260,3 +262,11 @@ def spec_accept_tree(batch, draft_len, vocab, logits, tokens, parents, target_to
                                  _ptr(out_tokens), _ptr(accept_path), _ptr(kv_lens_in),
                                  _ptr(kv_lens_out), _ptr(workspace), workspace_bytes,
                                  _stream(stream)))
+
+
+def spec_kv_commit_tree(params: SvAppendParams, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                        block_table, accept_path, kv_lens, stream=None) -> None:
+    _check(_lib.spec_kv_commit_tree(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(block_table), _ptr(accept_path), _ptr(kv_lens),
+                                    _stream(stream)))

@@ -291,13 +291,15 @@ sv_status spec_accept_sampled(int32_t batch, int32_t draft_len, int32_t vocab, f
   return SV_OK;
 }
 
-sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const void* v_new,
-                         void* k_cache, void* v_cache, float* k_scale, float* v_scale,
-                         const int32_t* block_table, const int32_t* kv_lens_in,
-                         int32_t* kv_lens_out, void* stream) {
+static sv_status run_append(const sv_append_params* p, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                            const int32_t* block_table, const int32_t* kv_lens_in,
+                            int32_t* kv_lens_out, const int32_t* path, void* stream) {
   if (!p) return fail(SV_ERR_INVALID, "params is NULL");
   if (p->batch < 1) return fail(SV_ERR_INVALID, "batch must be >= 1 (got %d)", p->batch);
   if (p->num_new < 1) return fail(SV_ERR_INVALID, "num_new must be >= 1 (got %d)", p->num_new);
+  if (path && p->num_new > 64)
+    return fail(SV_ERR_INVALID, "a tree has at most 64 nodes (num_new = %d)", p->num_new);
   if (p->num_kv_heads < 1) return fail(SV_ERR_INVALID, "num_kv_heads must be >= 1");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
@@ -313,12 +315,14 @@ sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const voi
     return fail(SV_ERR_INVALID, "num_new (%d) exceeds the table's %lld tokens", p->num_new,
                 (long long)p->max_blocks_per_seq * 16);
   const bool fp8 = p->kv_dtype == SV_KV_FP8_E4M3;
-  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !kv_lens_in || !kv_lens_out)
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !kv_lens_in ||
+      (!path && !kv_lens_out))
     return fail(SV_ERR_INVALID, "a required pointer is NULL");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(SV_ERR_INVALID, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
-  if (!aligned(block_table, 4) || !aligned(kv_lens_in, 4) || !aligned(kv_lens_out, 4))
-    return fail(SV_ERR_INVALID, "block_table and kv_lens must be 4-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(kv_lens_in, 4) || (kv_lens_out && !aligned(kv_lens_out, 4)) ||
+      (path && !aligned(path, 4)))
+    return fail(SV_ERR_INVALID, "block_table, kv_lens and accept_path must be 4-byte aligned");
   if (fp8) {
     if (!k_scale || !v_scale) return fail(SV_ERR_INVALID, "e4m3 caches need k_scale and v_scale");
     if (!aligned(k_scale, 4) || !aligned(v_scale, 4))
@@ -329,11 +333,28 @@ sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const voi
   sv::AppendPlan plan{p->batch, p->num_new, p->num_kv_heads, p->head_dim, p->max_blocks_per_seq,
                       p->num_blocks, fp8};
   hipError_t e = sv::launch_kv_append(plan, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
-                                      block_table, kv_lens_in, kv_lens_out,
+                                      block_table, kv_lens_in, kv_lens_out, path,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return SV_OK;
+}
+
+sv_status spec_kv_append(const sv_append_params* p, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* block_table, const int32_t* kv_lens_in,
+                         int32_t* kv_lens_out, void* stream) {
+  return run_append(p, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens_in,
+                    kv_lens_out, nullptr, stream);
+}
+
+sv_status spec_kv_commit_tree(const sv_append_params* p, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* block_table, const int32_t* accept_path,
+                              const int32_t* kv_lens, void* stream) {
+  if (!accept_path) return fail(SV_ERR_INVALID, "accept_path is NULL");
+  return run_append(p, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens,
+                    nullptr, accept_path, stream);
 }
 
 static sv_status check_draft_signals(int32_t rows, int32_t vocab, float temperature,

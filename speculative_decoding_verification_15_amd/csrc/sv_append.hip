@@ -20,6 +20,11 @@
 // x / scale, rounded to the nearest e4m3 value with ties to the even code and
 // magnitudes above 448 saturated; the sign bit is the quotient's.
 //
+// Tree commit (path != NULL): after a tree acceptance has committed the length
+// to L - R + AL, the accepted nodes' rows (path[1 .. AL-1]) are appended by the
+// same rule at positions length - (AL - 1) .., right behind the root; the
+// lengths are not written.
+//
 // Launch: one workgroup of 16 waves per sequence.  A wave takes one task at a
 // time: (block touched, KV head, K or V).  The workgroup reads kv_in[b] before
 // its barrier and one thread writes kv_out[b] after it, so kv_out may alias
@@ -43,9 +48,17 @@ struct AppendArgs {
   float* v_scale;
   const int32_t* table;    // [B][max_blocks]
   const int32_t* kv_in;
-  int32_t* kv_out;
+  int32_t* kv_out;         // NULL in the tree commit (lengths already committed)
+  const int32_t* path;     // tree commit: [B][R] accepted nodes, root first, -1 padded; else NULL
   int R, H_kv, hd, max_blocks, num_blocks;
 };
+
+// Row of k_new / v_new that the i-th appended position of sequence b takes:
+// i itself, or in the tree commit the (i + 1)-th accepted node.
+__device__ __forceinline__ int src_row(const AppendArgs& p, int b, int i) {
+  if (!p.path) return i;
+  return min(max(p.path[(size_t)b * p.R + 1 + i], 0), p.R - 1);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -138,7 +151,7 @@ __device__ void append_k_fp8(const AppendArgs& p, int b, int c, int P, int a, in
 #pragma unroll
       for (int i = 0; i < 16; ++i) hmax = fmaxf(hmax, fabsf(x[k][i]));
     } else if (isnew[k]) {
-      const uint16_t* src = p.k_new + (((size_t)b * p.R + (P + slot - c)) * p.H_kv + h) * HD + d16 * 16;
+      const uint16_t* src = p.k_new + (((size_t)b * p.R + src_row(p, b, P + slot - c)) * p.H_kv + h) * HD + d16 * 16;
       const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
       const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
 #pragma unroll
@@ -191,7 +204,7 @@ __device__ void append_v_fp8(const AppendArgs& p, int b, int c, int P, int a, in
       if (t < a) {
         hmax = fmaxf(hmax, fabsf(x[k][t]));
       } else if (t < a + n) {
-        x[k][t] = bf16_to_f32(p.v_new[(((size_t)b * p.R + (P + t - c)) * p.H_kv + h) * HD + d]);
+        x[k][t] = bf16_to_f32(p.v_new[(((size_t)b * p.R + src_row(p, b, P + t - c)) * p.H_kv + h) * HD + d]);
         nmax = fmaxf(nmax, fabsf(x[k][t]));
       }
     }
@@ -228,7 +241,7 @@ __device__ void append_k_bf16(const AppendArgs& p, int b, int c, int P, int a, i
   uint16_t* base = static_cast<uint16_t*>(p.k_cache) + (blk * p.H_kv + h) * (size_t)(HD * kBlock);
   for (int e = lane; e < n * V8; e += 64) {
     const int s = e / V8, d8 = e % V8;
-    const uint16_t* src = p.k_new + (((size_t)b * p.R + (P + a + s - c)) * p.H_kv + h) * HD + d8 * 8;
+    const uint16_t* src = p.k_new + (((size_t)b * p.R + src_row(p, b, P + a + s - c)) * p.H_kv + h) * HD + d8 * 8;
     *reinterpret_cast<u32x4*>(base + d8 * 128 + (a + s) * 8) = *reinterpret_cast<const u32x4*>(src);
   }
 }
@@ -242,7 +255,7 @@ __device__ void append_v_bf16(const AppendArgs& p, int b, int c, int P, int a, i
   for (int k = 0; k < HD / 64; ++k) {
     const int d = lane + 64 * k;
     for (int s = 0; s < n; ++s)
-      base[d * 16 + a + s] = p.v_new[(((size_t)b * p.R + (P + a + s - c)) * p.H_kv + h) * HD + d];
+      base[d * 16 + a + s] = p.v_new[(((size_t)b * p.R + src_row(p, b, P + a + s - c)) * p.H_kv + h) * HD + d];
   }
 }
 
@@ -252,8 +265,16 @@ __global__ __launch_bounds__(kAppendWaves * 64) void sv_kv_append(AppendArgs p) 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int cap = p.max_blocks * kBlock;
-  const int c = min(max(p.kv_in[b], 0), cap - p.R);   // in-bounds even for bad lengths
-  const int span = (p.R + 30) / kBlock;                 // most blocks [c, c + R) can touch
+  // rows appended: all R, or in the tree commit the accepted nodes after the
+  // root (up to the first -1), placed right behind the root
+  int rows = p.R;
+  if (p.path) {
+    rows = 0;
+    while (rows + 1 < p.R && p.path[(size_t)b * p.R + rows + 1] >= 0) ++rows;
+  }
+  const int start = p.path ? p.kv_in[b] - rows : p.kv_in[b];
+  const int c = min(max(start, 0), cap - rows);         // in-bounds even for bad lengths
+  const int span = (rows + 30) / kBlock;                // most blocks [c, c + rows) can touch
   const int tasks = span * p.H_kv * 2;
   for (int t = wave; t < tasks; t += kAppendWaves) {
     const int j = t / (2 * p.H_kv);
@@ -261,7 +282,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void sv_kv_append(AppendArgs p) 
     const bool is_v = t & 1;
     const int jb = c / kBlock + j;
     const int P = jb * kBlock;
-    const int lo = max(c, P), hi = min(c + p.R, P + kBlock);
+    const int lo = max(c, P), hi = min(c + rows, P + kBlock);
     if (lo >= hi) continue;
     const int a = lo - P;          // held slots 0 .. a-1 (non-zero only in the first block)
     const int n = hi - lo;         // new slots a .. a+n-1
@@ -276,7 +297,7 @@ __global__ __launch_bounds__(kAppendWaves * 64) void sv_kv_append(AppendArgs p) 
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) p.kv_out[b] = c + p.R;
+  if (threadIdx.x == 0 && p.kv_out) p.kv_out[b] = c + p.R;
 }
 
 }  // namespace
@@ -284,9 +305,9 @@ __global__ __launch_bounds__(kAppendWaves * 64) void sv_kv_append(AppendArgs p) 
 hipError_t launch_kv_append(const AppendPlan& pl, const void* k_new, const void* v_new,
                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                             const int32_t* table, const int32_t* kv_in, int32_t* kv_out,
-                            hipStream_t stream) {
+                            const int32_t* path, hipStream_t stream) {
   AppendArgs a{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-               k_cache, v_cache, k_scale, v_scale, table, kv_in, kv_out,
+               k_cache, v_cache, k_scale, v_scale, table, kv_in, kv_out, path,
                pl.R, pl.H_kv, pl.hd, pl.max_blocks, pl.num_blocks};
   const dim3 grid(pl.B), block(kAppendWaves * 64);
   if (pl.hd == 128) {

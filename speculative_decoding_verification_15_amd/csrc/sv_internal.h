@@ -60,6 +60,6 @@ struct AppendPlan {
 hipError_t launch_kv_append(const AppendPlan& plan, const void* k_new, const void* v_new,
                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                             const int32_t* table, const int32_t* kv_in, int32_t* kv_out,
-                            hipStream_t stream);
+                            const int32_t* path, hipStream_t stream);
 
 }  // namespace sv

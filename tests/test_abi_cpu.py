@@ -428,3 +428,20 @@ def test_accept_tree_errors(kw, status):
 
 def test_accept_tree_no_drafts_allows_null_tree():
     assert call_accept_tree(D=0, tok=None, par=None, ws=None) == sv.SV_ERR_WORKSPACE
+
+
+def test_commit_tree_errors():
+    lib = sv.library()
+
+    def call(path=FAKE, kvl=FAKE, **kw):
+        shape = dict(batch=4, num_new=16, num_kv_heads=8, head_dim=128, max_blocks_per_seq=64,
+                     num_blocks=256)
+        shape.update(kw)
+        p = sv.make_append_params(**shape)
+        return lib.spec_kv_commit_tree(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                                       path, kvl, None)
+    assert call(path=None) == sv.SV_ERR_INVALID
+    assert call(path=FAKE + 2) == sv.SV_ERR_INVALID
+    assert call(kvl=None) == sv.SV_ERR_INVALID
+    assert call(num_new=65) == sv.SV_ERR_INVALID
+    assert call(head_dim=80) == sv.SV_ERR_UNSUPPORTED

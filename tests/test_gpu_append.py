@@ -193,3 +193,47 @@ def test_append_full_size(w):
     got = gpu_append(*args)
     want = oracle_kv_append(*args)
     assert_same(got, want, w.name)
+
+
+def gpu_commit(k_new, v_new, k_cache, v_cache, k_scale, v_scale, table, lens, path, fp8):
+    B, R, H, hd = k_new.shape
+    note(f"[gpu] spec_kv_commit_tree B={B} R={R} fp8={fp8}")
+    kc, vc = dev(k_cache), dev(v_cache)
+    ks = dev(k_scale) if fp8 else None
+    vs = dev(v_scale) if fp8 else None
+    kl = dev(np.asarray(lens, np.int32))
+    p = sv.make_append_params(batch=B, num_new=R, num_kv_heads=H, head_dim=hd,
+                              max_blocks_per_seq=table.shape[1], num_blocks=k_cache.shape[0],
+                              kv_dtype=sv.SV_KV_FP8_E4M3 if fp8 else sv.SV_KV_BF16)
+    sv.spec_kv_commit_tree(p, dev(k_new), dev(v_new), kc, vc, ks, vs, dev(table),
+                           dev(np.asarray(path, np.int32)), kl)
+    torch.cuda.synchronize()
+    return (_host(kc, k_cache), _host(vc, v_cache), _host(ks, k_scale) if fp8 else None,
+            _host(vs, v_scale) if fp8 else None, kl.cpu().numpy())
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_tree_commit_matches_oracle_bytes(fp8, seed):
+    from tests.test_oracle_append import _tree_step
+    st = _tree_step(fp8, seed=seed)
+    acc = st["acc"]
+    args = (st["k_new"], st["v_new"], st["kc"], st["vc"], st["ks"], st["vs"], st["table"],
+            acc["kv_lens_out"])
+    want = oracle_kv_append(*args, fp8, accept_path=acc["accept_path"])
+    got = gpu_commit(*args, acc["accept_path"], fp8)
+    assert_same(got, want, f"tree commit fp8={fp8} seed={seed}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_tree_commit_chain_and_empty_paths(fp8):
+    from tests.test_oracle_append import _tree_step
+    st = _tree_step(fp8)
+    path = np.full((3, 16), -1, np.int32)
+    path[0, :16] = np.arange(16)          # every node of a chain
+    path[1, :1] = 0                       # root only: nothing to move
+    path[2, :4] = [0, 2, 5, 9]
+    lens = st["T"] + np.array([16, 1, 4], np.int32)
+    args = (st["k_new"], st["v_new"], st["kc"], st["vc"], st["ks"], st["vs"], st["table"], lens)
+    want = oracle_kv_append(*args, fp8, accept_path=path)
+    assert_same(gpu_commit(*args, path, fp8), want, f"chain/empty fp8={fp8}")
