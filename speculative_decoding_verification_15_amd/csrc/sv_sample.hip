@@ -33,6 +33,13 @@
 
 namespace sv {
 
+// x / tau; with UNIT_TAU (tau == 1) the division, exact then, is left out.
+template <bool UNIT_TAU>
+__device__ __forceinline__ float over_tau(float x, float tau) {
+  if constexpr (UNIT_TAU) return x;
+  else return x / tau;
+}
+
 struct SampleStat {
   float m;       // chunk maximum (-inf: nothing finite in the chunk)
   float pad;
@@ -60,7 +67,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 // grid = (chunks, B * (1 + D) + B * D); rows below rows_t are target rows
 // (b * R + j), the others draft rows (b * D + j).  VEC: V % 4 == 0, so rows
 // start 16-byte aligned and whole float4 loads are used.
-template <bool VEC>
+template <bool VEC, bool UNIT_TAU>
 __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_stats(
     const float* __restrict__ zt, const float* __restrict__ zd, int rows_t, int V, int chunks,
     float tau, SampleStat* __restrict__ st) {
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_stats(
   double s = 0.0;
   if (m != -INFINITY) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) s += (double)expf((v[u] - m) / tau);
+    for (int u = 0; u < U; ++u) s += (double)expf(over_tau<UNIT_TAU>(v[u] - m, tau));
   }
   s = wave_sum(s);
   if (t % kWave == 0) red_s[t / kWave] = s;
@@ -128,24 +135,28 @@ struct DrawInfo {
 // exponentials (correctly rounded division, accurate exp) times an fp64 1 / S:
 // a rounded fp32 1 / S would scale all of p, or all of q, by one factor and move
 // every boundary of the residual together.
+template <bool UNIT_TAU = false>
 __device__ __forceinline__ double weight_p(float z, const DrawInfo& d, float tau) {
-  return (double)expf((z - d.Mp) / tau) * d.invSp;
+  return (double)expf(over_tau<UNIT_TAU>(z - d.Mp, tau)) * d.invSp;
 }
+template <bool UNIT_TAU = false>
 __device__ __forceinline__ double weight_r(float z, float y, const DrawInfo& d, float tau) {
-  const double q = (double)expf((y - d.Mq) / tau) * d.invSq;
-  return fmax(weight_p(z, d, tau) - q, 0.0);
+  const double q = (double)expf(over_tau<UNIT_TAU>(y - d.Mq, tau)) * d.invSq;
+  return fmax(weight_p<UNIT_TAU>(z, d, tau) - q, 0.0);
 }
 
-// grid = B, 256 threads: row normalisers (max M over the chunks and
+// grid = B, 1024 threads: row normalisers (max M over the chunks and
 // S = sum_c s_c e^((m_c - M) / tau)), the keep tests in order, and every output
 // but the emitted token.
-__global__ __launch_bounds__(kArgmaxThreads) void sv_sample_keep(
+constexpr int kKeepThreads = 1024;   // 16 waves: the row normalisers of up to 127 rows, 8 per wave
+
+__global__ __launch_bounds__(kKeepThreads) void sv_sample_keep(
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ draft,
     const float* __restrict__ u_accept, int D, int V, int chunks, float tau,
     const SampleStat* __restrict__ st, DrawInfo* __restrict__ info,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens,
     const int32_t* __restrict__ kv_in, int32_t* __restrict__ kv_out) {
-  constexpr int kThreads = kArgmaxThreads;
+  constexpr int kThreads = kKeepThreads;
   __shared__ float s_M[2 * 64 + 1];         // per row r: target rows 0 .. D, draft rows R + j
   __shared__ double s_S[2 * 64 + 1];
   __shared__ bool s_keep[64];
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_keep(
 // 4096-logit chunk of the emitted token's row, read coalesced.  Per chunk:
 // {sum of the drawn weights, sum of p_n} (the second serves when the residual is
 // zero everywhere, p_n == q_n).
-template <bool VEC>
+template <bool VEC, bool UNIT_TAU>
 __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_chunk_sums(
     const float* __restrict__ zt, const float* __restrict__ zd, int D, int V, int chunks,
     float tau, const DrawInfo* __restrict__ info, double2* __restrict__ sums) {
@@ -238,9 +249,9 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_chunk_sums(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (z4[e] == -INFINITY) continue;
-        const double p = weight_p(z4[e], di, tau);
+        const double p = weight_p<UNIT_TAU>(z4[e], di, tau);
         sp += p;
-        sw += di.resid ? weight_r(z4[e], y4[e], di, tau) : p;
+        sw += di.resid ? weight_r<UNIT_TAU>(z4[e], y4[e], di, tau) : p;
       }
     }
   } else {
@@ -248,9 +259,9 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_chunk_sums(
     for (int u = 0; u < U; ++u) {
       const int i = base + u * kArgmaxThreads + t;
       if (i >= V || zr[i] == -INFINITY) continue;
-      const double p = weight_p(zr[i], di, tau);
+      const double p = weight_p<UNIT_TAU>(zr[i], di, tau);
       sp += p;
-      sw += di.resid ? weight_r(zr[i], yr[i], di, tau) : p;
+      sw += di.resid ? weight_r<UNIT_TAU>(zr[i], yr[i], di, tau) : p;
     }
   }
   sw = wave_sum(sw);
@@ -282,6 +293,8 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_draw(
     const double2* __restrict__ sums, int32_t* __restrict__ out_tokens) {
   constexpr int kThreads = kArgmaxThreads;
   constexpr int kPer = kArgmaxChunk / kThreads;      // 16 logits per thread
+  constexpr int kStagedChunks = 1024;              // vocabularies up to 4M logits
+  __shared__ double2 s_sums[kStagedChunks];
   __shared__ double s_own[kThreads], s_part[kThreads];
   __shared__ double s_off;
   __shared__ int s_chunk, s_tok, s_resid, s_sel;
@@ -289,19 +302,26 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_draw(
   const int R = D + 1;
   const int t = threadIdx.x;
   DrawInfo di = info[b];
+  // the chunk sums, staged in LDS by all threads (one global round trip),
+  // then summed by thread 0 in chunk order
+  const double2* sb = sums + (size_t)b * chunks;
+  const bool staged = chunks <= kStagedChunks;
+  if (staged)
+    for (int c = t; c < chunks; c += kThreads) s_sums[c] = sb[c];
+  __syncthreads();
+  auto chunk_sum = [&](int c) -> double2 { return staged ? s_sums[c] : sb[c]; };
   if (t == 0) {
-    const double2* sb = sums + (size_t)b * chunks;
     double tot_w = 0.0;
-    for (int c = 0; c < chunks; ++c) tot_w += sb[c].x;
+    for (int c = 0; c < chunks; ++c) tot_w += chunk_sum(c).x;
     const bool use_w = !(di.resid && tot_w == 0.0);   // p_n == q_n: draw from p_n
     double total = 0.0;
-    for (int c = 0; c < chunks; ++c) total += use_w ? sb[c].x : sb[c].y;
+    for (int c = 0; c < chunks; ++c) total += use_w ? chunk_sum(c).x : chunk_sum(c).y;
     const double T = (double)u_sample[b] * total;
     double run = 0.0;
     int pick = -1, last = 0;
     double off = 0.0, last_off = 0.0;
     for (int c = 0; c < chunks; ++c) {
-      const double w = use_w ? sb[c].x : sb[c].y;
+      const double w = use_w ? chunk_sum(c).x : chunk_sum(c).y;
       if (w > 0.0) {
         last = c;
         last_off = run;
@@ -377,27 +397,39 @@ hipError_t launch_accept_sampled(int B, int D, int V, float tau, const float* zt
   const int chunks = argmax_chunks(V);
   auto* st = static_cast<SampleStat*>(ws);
   dim3 grid(chunks, B * (R + D));
-  if (V % 4 == 0)
-    sv_sample_stats<true><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
+  // tau == 1: the exact division by tau is left out of the per-logit work
+  const bool unit = tau == 1.f;
+  if (V % 4 == 0 && unit)
+    sv_sample_stats<true, true><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
+  else if (V % 4 == 0)
+    sv_sample_stats<true, false><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
+  else if (unit)
+    sv_sample_stats<false, true><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
   else
-    sv_sample_stats<false><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
+    sv_sample_stats<false, false><<<grid, kArgmaxThreads, 0, stream>>>(zt, zd, B * R, V, chunks, tau, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // workspace after the chunk statistics: DrawInfo[B], then {sum w, sum p}[B][chunks]
   const size_t st_bytes = (size_t)B * (R + D) * chunks * sizeof(SampleStat);
   auto* info = reinterpret_cast<DrawInfo*>(static_cast<char*>(ws) + st_bytes);
   auto* sums = reinterpret_cast<double2*>(static_cast<char*>(ws) + st_bytes + (size_t)B * sizeof(DrawInfo));
-  sv_sample_keep<<<B, kArgmaxThreads, 0, stream>>>(zt, zd, draft, u_accept, D, V, chunks, tau, st,
+  sv_sample_keep<<<B, kKeepThreads, 0, stream>>>(zt, zd, draft, u_accept, D, V, chunks, tau, st,
                                                    info, accept_len, out_tokens, kv_in, kv_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid3(chunks, B);
-  if (V % 4 == 0)
-    sv_sample_chunk_sums<true><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks, tau,
-                                                                     info, sums);
+  if (V % 4 == 0 && unit)
+    sv_sample_chunk_sums<true, true><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks,
+                                                                           tau, info, sums);
+  else if (V % 4 == 0)
+    sv_sample_chunk_sums<true, false><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks,
+                                                                            tau, info, sums);
+  else if (unit)
+    sv_sample_chunk_sums<false, true><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks,
+                                                                            tau, info, sums);
   else
-    sv_sample_chunk_sums<false><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks, tau,
-                                                                      info, sums);
+    sv_sample_chunk_sums<false, false><<<grid3, kArgmaxThreads, 0, stream>>>(zt, zd, D, V, chunks,
+                                                                             tau, info, sums);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   sv_sample_draw<<<B, kArgmaxThreads, 0, stream>>>(zt, zd, u_sample, D, V, chunks, tau, info, sums,
