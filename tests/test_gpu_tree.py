@@ -170,3 +170,64 @@ def test_tree_accept_70b_like():
     for k in want:
         assert np.array_equal(got[k], want[k]), k
     assert want["accept_len"].max() > 2
+
+
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15"])
+def test_tree_step_on_device_end_to_end(name):
+    """spec_kv_append -> spec_verify_attn_tree -> spec_accept_tree -> spec_kv_commit_tree
+    on the device, lengths passed from call to call on the device, against the
+    oracle's four steps: attention within tolerance, everything else bit-exact."""
+    from oracle.append import oracle_kv_append
+    from workloads import make_append_inputs
+    w = MINI[name]
+    fp8 = w.kv_dtype == "fp8_e4m3"
+    ap = make_append_inputs(w, gains=(0.5, 1.0, 2.0))
+    b = ap.base
+    tp = make_tree_plan(w, shape="random", width=3, p_match=0.8)
+    plan_l = make_accept_plan(w)
+    tok = tree_tokens_from_target(tp, oracle_argmax(plan_l.logits))
+    # oracle chain
+    rk, rv, rks, rvs, L = oracle_kv_append(ap.k_new, ap.v_new, b.k_cache, b.v_cache, b.k_scale,
+                                           b.v_scale, b.block_table, ap.committed, fp8)
+    o_ref = oracle_attn(b.q, rk, rv, rks, rvs, b.block_table, L, D=w.D, H_kv=w.H_kv,
+                        sm_scale=w.sm_scale, parents=tp.parents)
+    acc = oracle_accept_tree(plan_l.logits, tok, tp.parents, L)
+    ck, cv, cks, cvs, cl = oracle_kv_append(ap.k_new, ap.v_new, rk, rv, rks, rvs, b.block_table,
+                                            acc["kv_lens_out"], fp8, accept_path=acc["accept_path"])
+    # device chain
+    note(f"[gpu] tree step {name}")
+    d = DeviceAttn(b)
+    lens = dev(ap.committed)
+    kn, vn = dev(ap.k_new), dev(ap.v_new)
+    ap_p = sv.make_append_params(batch=w.B, num_new=w.R, num_kv_heads=w.H_kv, head_dim=w.hd,
+                                 max_blocks_per_seq=b.block_table.shape[1], num_blocks=b.num_blocks,
+                                 kv_dtype=sv.SV_KV_FP8_E4M3 if fp8 else sv.SV_KV_BF16)
+    sv.spec_kv_append(ap_p, kn, vn, d.k, d.v, d.ks, d.vs, d.bt, lens, lens)
+    d.kl = lens
+    p = attn_params(b)
+    ws_bytes = sv.spec_verify_attn_workspace_size(p)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.full(d.q.shape, int(BF16_NAN), dtype=torch.int16, device="cuda")
+    tm = torch.from_numpy(np.ascontiguousarray(tp.masks).view(np.int64)).cuda()
+    sv.spec_verify_attn_tree(p, d.q, d.k, d.v, d.ks, d.vs, d.bt, lens, tm, out, ws, ws_bytes)
+    B, R, V = w.B, w.R, w.V
+    outs = {k: torch.full(s, -7, dtype=torch.int32, device="cuda") for k, s in
+            (("target", (B, R)), ("accept_len", (B,)), ("out_tokens", (B, R)),
+             ("accept_path", (B, R)))}
+    aws_bytes = sv.spec_accept_workspace_size(B, w.D, V)
+    aws = torch.empty(aws_bytes, dtype=torch.uint8, device="cuda")
+    sv.spec_accept_tree(B, w.D, V, dev(plan_l.logits), dev(tok), dev(tp.parents), outs["target"],
+                        outs["accept_len"], outs["out_tokens"], outs["accept_path"], lens, lens,
+                        aws, aws_bytes)
+    sv.spec_kv_commit_tree(ap_p, kn, vn, d.k, d.v, d.ks, d.vs, d.bt, outs["accept_path"], lens)
+    torch.cuda.synchronize()
+    _check(DeviceAttn.to_f64(out), o_ref, f"{name}/tree step")
+    for k in ("target", "accept_len", "out_tokens", "accept_path"):
+        assert np.array_equal(outs[k].cpu().numpy(), acc[k]), k
+    assert np.array_equal(lens.cpu().numpy(), cl)
+    k_got = d.k.cpu().numpy().view(ck.dtype)
+    v_got = d.v.cpu().numpy().view(cv.dtype)
+    assert np.array_equal(k_got, ck) and np.array_equal(v_got, cv)
+    if fp8:
+        assert np.array_equal(d.ks.cpu().numpy().view(np.uint32), cks.view(np.uint32))
+        assert np.array_equal(d.vs.cpu().numpy().view(np.uint32), cvs.view(np.uint32))
