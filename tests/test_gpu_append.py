@@ -133,7 +133,7 @@ def test_append_chain_from_empty_cache(fp8, hd):
              for _ in range(2)]
     kc, vc, ks, vs, _ = oracle_kv_append(*first, kc, vc, ks, vs, table, np.zeros(B, np.int32), fp8)
     lens = np.array([16, 5, 15], np.int32)
-    for step, R in enumerate((1, 7, 16, 3, 33, 16, 9)):
+    for step, R in enumerate((1, 7, 16, 3, 33, 16, 9, 200)):   # 200: a prefill-sized append
         gain = np.float32(rng.choice([0.05, 1.0, 2.0, 40.0]))
         k = f32_to_bf16_bits(rng.standard_normal((B, R, H, hd), dtype=np.float32) * gain)
         v = f32_to_bf16_bits(rng.standard_normal((B, R, H, hd), dtype=np.float32) * gain)
