@@ -96,6 +96,24 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_argmax_partial(
   }
 }
 
+// (max, lowest index) over the chunk results p[0 .. chunks) of one row.  The
+// loads go out sixteen at a time (past the end the last chunk is read again,
+// which cannot change the result), so the reduction waits for one round trip
+// per sixteen chunks rather than one per chunk.
+__device__ __forceinline__ int reduce_parts(const ArgmaxPart* __restrict__ p, int chunks) {
+  constexpr int kBatch = 16;
+  float bv = -INFINITY;
+  int bi = INT32_MAX;
+  for (int c0 = 0; c0 < chunks; c0 += kBatch) {
+    ArgmaxPart q[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) q[k] = p[min(c0 + k, chunks - 1)];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) consider(q[k].value, q[k].index, bv, bi);
+  }
+  return bi;
+}
+
 // grid = B; one wave per sequence; lane j handles row j (R <= 64).
 __global__ __launch_bounds__(kWave) void sv_accept_finalize(
     const ArgmaxPart* __restrict__ part, int chunks, int D, const int32_t* __restrict__ draft,
@@ -106,11 +124,7 @@ __global__ __launch_bounds__(kWave) void sv_accept_finalize(
   const int R = D + 1;
   int tok = 0;
   if (j < R) {
-    const ArgmaxPart* p = part + ((size_t)b * R + j) * chunks;
-    float bv = -INFINITY;
-    int bi = INT32_MAX;
-    for (int c = 0; c < chunks; ++c) consider(p[c].value, p[c].index, bv, bi);
-    tok = bi;
+    tok = reduce_parts(part + ((size_t)b * R + j) * chunks, chunks);
     target[(size_t)b * R + j] = tok;
   }
   const bool mismatch = (j < D) && (draft[(size_t)b * D + j] != tok);
@@ -144,11 +158,7 @@ __global__ __launch_bounds__(kWave) void sv_accept_tree_finalize(
   const int j = threadIdx.x;
   int a = 0, par = -2, tok = -1;
   if (j < R) {
-    const ArgmaxPart* p = part + ((size_t)b * R + j) * chunks;
-    float bv = -INFINITY;
-    int bi = INT32_MAX;
-    for (int c = 0; c < chunks; ++c) consider(p[c].value, p[c].index, bv, bi);
-    a = bi;
+    a = reduce_parts(part + ((size_t)b * R + j) * chunks, chunks);
     target[(size_t)b * R + j] = a;
     if (j > 0) {
       par = parents[(size_t)b * R + j];
