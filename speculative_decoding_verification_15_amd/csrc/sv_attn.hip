@@ -261,10 +261,10 @@ __device__ __forceinline__ bool softmax_core(f32x16 (&x)[2], const float (&cs)[2
 template <bool MASKED = false>
 __device__ __forceinline__ bool softmax_sub(const f32x16& x, float c, float& m_ref, float& l_run,
                                             float& alpha, bf16x8& p0, bf16x8& p1) {
-  float hm = x[0];
+  float hm = fmaximum(x[0], x[1]);
 #pragma unroll
-  for (int v = 1; v < 16; ++v) hm = fmaxf(hm, x[v]);
-  const float tmax = halves_max(hm * c);
+  for (int v = 2; v < 16; ++v) hm = fmaximum(hm, x[v]);
+  const float tmax = halves_maximum(hm * c);
   // Selects rather than branches, so that the caller can overlap this VALU
   // work with MFMAs of its own basic block.
   const bool first = m_ref == -INFINITY;     // no visible key yet: O and l are 0
@@ -299,10 +299,10 @@ __device__ __forceinline__ bool softmax_sub_fp8(const f32x16& x, float c0, float
   float h0 = x[0], h1 = x[8];
 #pragma unroll
   for (int v = 1; v < 8; ++v) {
-    h0 = fmaxf(h0, x[v]);
-    h1 = fmaxf(h1, x[8 + v]);
+    h0 = fmaximum(h0, x[v]);
+    h1 = fmaximum(h1, x[8 + v]);
   }
-  const float tmax = halves_max(fmaxf(h0 * c0, h1 * c1));
+  const float tmax = halves_maximum(fmaximum(h0 * c0, h1 * c1));
   const bool first = m_ref == -INFINITY;
   const bool move = !first && tmax > m_ref + kLazyRescale;
   alpha = move ? fast_exp2(m_ref - tmax) : 1.f;

@@ -36,6 +36,16 @@ __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// IEEE maximum (NaN-propagating) of the lane pair (l, l ^ 32) and of three
+// values: unlike fmaxf they need no quieting of their inputs (which the compiler
+// otherwise adds for values it cannot prove canonical, such as MFMA results and
+// permlane outputs), and gfx950 has a three-input form.  For the softmax's
+// maxima, whose inputs are finite or -inf, the result is the same.
+__device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float halves_maximum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
