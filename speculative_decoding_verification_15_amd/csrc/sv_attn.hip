@@ -288,6 +288,42 @@ __device__ __forceinline__ bool softmax_sub(const f32x16& x, float c, float& m_r
   return __ballot(move) != 0;
 }
 
+// Running maximum of a stream-K segment before its first visible key: finite,
+// so that the first tile with one simply moves the reference (alpha = 0 then
+// scales O and l, both still 0) and no per-tile test for a first key is
+// needed.  A tile whose keys are all masked leaves it there (its scores are
+// -inf, exp2(-inf + 1e30) = 0), and a segment that never sees a key stores
+// m = kNoMax with l = 0, which the merge weighs by 0.
+constexpr float kNoMax = -1e30f;
+
+// softmax_sub for the stream-K kernels (running maximum starting at kNoMax).
+__device__ __forceinline__ bool softmax_sub_sk(const f32x16& x, float c, float& m_ref,
+                                               float& l_run, float& alpha, bf16x8& p0,
+                                               bf16x8& p1) {
+  float hm = fmaximum(x[0], x[1]);
+#pragma unroll
+  for (int v = 2; v < 16; ++v) hm = fmaximum(hm, x[v]);
+  const float tmax = halves_maximum(hm * c);
+  const bool move = tmax > m_ref + kLazyRescale;
+  alpha = move ? fast_exp2(m_ref - tmax) : 1.f;
+  m_ref = move ? tmax : m_ref;
+  const float m_neg = -m_ref;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p0[j] = (__bf16)fast_exp2(__builtin_fmaf(x[j], c, m_neg));
+    p1[j] = (__bf16)fast_exp2(__builtin_fmaf(x[8 + j], c, m_neg));
+  }
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[j], p0[j + 1]}, one, psum, false);
+    psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[j], p1[j + 1]}, one, psum, false);
+  }
+  l_run = l_run * alpha + psum;
+  return __ballot(move) != 0;
+}
+
 // softmax_sub for a tile decoded from e4m3 codes: the scores of key block b
 // (16 keys: registers 8b .. 8b + 7) are scaled by cb = c * (K mantissa of
 // block b), and the probabilities of block b are returned times the block's V
@@ -303,11 +339,10 @@ __device__ __forceinline__ bool softmax_sub_fp8(const f32x16& x, float c0, float
     h1 = fmaximum(h1, x[8 + v]);
   }
   const float tmax = halves_maximum(fmaximum(h0 * c0, h1 * c1));
-  const bool first = m_ref == -INFINITY;
-  const bool move = !first && tmax > m_ref + kLazyRescale;
+  const bool move = tmax > m_ref + kLazyRescale;   // the running maximum starts at kNoMax
   alpha = move ? fast_exp2(m_ref - tmax) : 1.f;
-  m_ref = (first || move) ? tmax : m_ref;
-  const float m_neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+  m_ref = move ? tmax : m_ref;
+  const float m_neg = -m_ref;
   const float a0 = m_neg + __builtin_amdgcn_logf(mv0), a1 = m_neg + __builtin_amdgcn_logf(mv1);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -1243,7 +1278,7 @@ void sv_attn_streamk(AttnArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   f32x16 xn;                                   // scores of tile g + 1, when have_xn
   bool have_xn = false;
-  float m_ref = -INFINITY, l_run = 0.f;
+  float m_ref = kNoMax, l_run = 0.f;
   for (int g = g0; g < g1; ++g) {
     const unsigned t = (unsigned)(g - g0);    // unsigned: stage indices are cheap remainders
     // This wave's loads of tiles g and g + 1 landed: loads retire in issue
@@ -1262,7 +1297,7 @@ void sv_attn_streamk(AttnArgs a) {
       for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-      m_ref = -INFINITY;
+      m_ref = kNoMax;
       l_run = 0.f;
       have_xn = false;
     }
@@ -1300,7 +1335,7 @@ void sv_attn_streamk(AttnArgs a) {
       sk_read_v<HD>(stage, v_lds, vop);
       float alpha;
       bf16x8 p[2];
-      const bool rescale = softmax_sub<true>(x, a.c, m_ref, l_run, alpha, p[0], p[1]);
+      const bool rescale = softmax_sub_sk(x, a.c, m_ref, l_run, alpha, p[0], p[1]);
       // Keep the probabilities and V operands in this block (ahead of the
       // rescale branch), and interleave: the next tile's K reads and this
       // tile's V reads first, then each of the next tile's score MFMAs
@@ -1518,7 +1553,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   f32x16 xn;                                   // scores of tile g + 1, when have_xn
   bool have_xn = false;
-  float m_ref = -INFINITY, l_run = 0.f;
+  float m_ref = kNoMax, l_run = 0.f;
   int i0 = 0, i1 = 1, i2 = 2;
   for (int g = g0; g < g1; ++g) {
     // this wave's codes of tile g + 2 landed (tiles g + 3, g + 4 may not have:
@@ -1537,7 +1572,7 @@ void sv_attn_streamk_fp8(AttnArgs a) {
       for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-      m_ref = -INFINITY;
+      m_ref = kNoMax;
       l_run = 0.f;
       have_xn = false;
     }
