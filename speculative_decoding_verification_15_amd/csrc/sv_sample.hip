@@ -345,12 +345,35 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_draw(
   const float* zr = zt + ((size_t)b * R + di.n) * V;
   const float* yr = di.resid ? zd + ((size_t)b * D + di.n) * V : zr;
   const int v0 = min(chunk * kArgmaxChunk + t * kPer, V), v1 = min(v0 + kPer, V);
-  auto weight = [&](int v) -> double {
-    if (zr[v] == -INFINITY) return 0.0;
-    return di.resid ? weight_r(zr[v], yr[v], di, tau) : weight_p(zr[v], di, tau);
-  };
+  // this thread's logits, loaded together (16-byte vectors where the row
+  // allows; -inf past its end), and their weights, kept for the walk below
+  float zv[kPer], yv[kPer];
+  if (V % 4 == 0 && v1 - v0 == kPer) {
+#pragma unroll
+    for (int k = 0; k < kPer; k += 4) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(zr + v0 + k);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(yr + v0 + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zv[k + e] = a4[e];
+        yv[k + e] = b4[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      zv[k] = v0 + k < v1 ? zr[v0 + k] : -INFINITY;
+      yv[k] = v0 + k < v1 ? yr[v0 + k] : -INFINITY;
+    }
+  }
+  double wv[kPer];
   double own = 0.0;
-  for (int v = v0; v < v1; ++v) own += weight(v);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    wv[k] = zv[k] == -INFINITY ? 0.0
+                               : (di.resid ? weight_r(zv[k], yv[k], di, tau) : weight_p(zv[k], di, tau));
+    own += wv[k];
+  }
   s_own[t] = own;
   __syncthreads();
   if (t == 0) {
@@ -373,12 +396,14 @@ __global__ __launch_bounds__(kArgmaxThreads) void sv_sample_draw(
   if (t == s_sel) {
     double run = s_part[t];
     int tok = -1, last = -1;
-    for (int v = v0; v < v1; ++v) {
-      const double w = weight(v);
-      if (w > 0.0) last = v;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (v0 + k >= v1) break;
+      const double w = wv[k];
+      if (w > 0.0) last = v0 + k;
       run += w;
       if (run > Tc) {
-        tok = v;
+        tok = v0 + k;
         break;
       }
     }
