@@ -234,29 +234,49 @@ __device__ void append_v_fp8(const AppendArgs& p, int b, int c, int P, int a, in
 }
 
 // bf16 K block [hd/8][16 slots][8 dims]: one 16-byte vector per (new slot, 8 dims).
+// Every load is issued before the first store (fixed trip counts, guarded), so
+// a task costs one memory round trip rather than one per vector.
 template <int HD>
 __device__ void append_k_bf16(const AppendArgs& p, int b, int c, int P, int a, int n, size_t blk,
                               int h, int lane) {
   constexpr int V8 = HD / 8;
+  constexpr int IT = kBlock * V8 / 64;       // vectors per lane for a full block
   uint16_t* base = static_cast<uint16_t*>(p.k_cache) + (blk * p.H_kv + h) * (size_t)(HD * kBlock);
-  for (int e = lane; e < n * V8; e += 64) {
-    const int s = e / V8, d8 = e % V8;
-    const uint16_t* src = p.k_new + (((size_t)b * p.R + src_row(p, b, P + a + s - c)) * p.H_kv + h) * HD + d8 * 8;
-    *reinterpret_cast<u32x4*>(base + d8 * 128 + (a + s) * 8) = *reinterpret_cast<const u32x4*>(src);
+  u32x4 val[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = lane + 64 * i, s = e / V8, d8 = e % V8;
+    if (s < n)
+      val[i] = *reinterpret_cast<const u32x4*>(
+          p.k_new + (((size_t)b * p.R + src_row(p, b, P + a + s - c)) * p.H_kv + h) * HD + d8 * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = lane + 64 * i, s = e / V8, d8 = e % V8;
+    if (s < n) *reinterpret_cast<u32x4*>(base + d8 * 128 + (a + s) * 8) = val[i];
   }
 }
 
-// bf16 V block [hd][16 slots]: lane owns dims d = lane + 64 k, one 2-byte store per new slot.
+// bf16 V block [hd][16 slots]: lane owns dims d = lane + 64 k, one 2-byte store per new slot;
+// all loads first, as for K.
 template <int HD>
 __device__ void append_v_bf16(const AppendArgs& p, int b, int c, int P, int a, int n, size_t blk,
                               int h, int lane) {
   uint16_t* base = static_cast<uint16_t*>(p.v_cache) + (blk * p.H_kv + h) * (size_t)(HD * kBlock);
+  uint16_t val[HD / 64][kBlock];
 #pragma unroll
-  for (int k = 0; k < HD / 64; ++k) {
-    const int d = lane + 64 * k;
-    for (int s = 0; s < n; ++s)
-      base[d * 16 + a + s] = p.v_new[(((size_t)b * p.R + src_row(p, b, P + a + s - c)) * p.H_kv + h) * HD + d];
+  for (int s = 0; s < kBlock; ++s) {
+    if (s < n) {
+      const uint16_t* src = p.v_new + (((size_t)b * p.R + src_row(p, b, P + a + s - c)) * p.H_kv + h) * HD;
+#pragma unroll
+      for (int k = 0; k < HD / 64; ++k) val[k][s] = src[lane + 64 * k];
+    }
   }
+#pragma unroll
+  for (int k = 0; k < HD / 64; ++k)
+#pragma unroll
+    for (int s = 0; s < kBlock; ++s)
+      if (s < n) base[(lane + 64 * k) * 16 + a + s] = val[k][s];
 }
 
 template <int HD, bool FP8>
