@@ -1,7 +1,8 @@
 """The verification step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
 
 The library allocates nothing and records no memset, so a serving loop can
-capture spec_kv_append -> spec_verify_attn -> spec_accept once and replay it.
+capture spec_kv_append -> spec_verify_attn -> spec_accept once and replay it
+(and likewise spec_accept_sampled and spec_draft_signals).
 Each replay, with eager work and synchronisations between replays, must give
 the eager step's outputs bit for bit (the kernels are deterministic).
 """
@@ -85,6 +86,73 @@ def test_step_in_a_graph_replays_like_eager(name):
         al.fill_(-1)
         torch.cuda.synchronize()
         note(f"[gpu] graph step {name}: replay {rep}")
+        g.replay()
+        got = snapshot()
+        for i, (x, y) in enumerate(zip(got, want)):
+            assert np.array_equal(x, y), (rep, i)
+
+
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_hd64_g4"])
+def test_sampled_acceptance_and_draft_signals_in_a_graph(name):
+    """spec_accept_sampled (four kernels over a workspace) and spec_draft_signals
+    (two) captured together; every replay gives the eager outputs bit for bit."""
+    from workloads import make_draft_logits, make_sampled_accept_inputs
+    w = MINI[name]
+    si = make_sampled_accept_inputs(w)
+    B, D, V, R = w.B, w.D, w.V, w.R
+    zt, zd = dev(si.target_logits), dev(si.draft_logits)
+    dr, ua, us = dev(si.draft), dev(si.u_accept), dev(si.u_sample)
+    kin = torch.full((B,), 5000, dtype=torch.int32, device="cuda")
+    kout = torch.empty_like(kin)
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    otok = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    ws_bytes = sv.spec_accept_sampled_workspace_size(B, D, V)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    rows = 2 * B
+    dl = dev(make_draft_logits(rows, V, seed=7))
+    conf = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    ent = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    nlen = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    dws_bytes = sv.spec_draft_signals_workspace_size(rows, V)
+    dws = torch.empty(dws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step(stream):
+        sv.spec_accept_sampled(B, D, V, si.tau, zt, zd, dr, ua, us, al, otok, kin, kout, ws,
+                               ws_bytes, stream=stream)
+        sv.spec_draft_signals(rows, V, 1.0, dl, conf, ent, nlen, 15, 0.05, w.H_q // w.H_kv, dws,
+                              dws_bytes, stream=stream)
+
+    def clear():
+        for t in (al, otok, kout, nlen):
+            t.fill_(-7)
+        conf.fill_(-1.0)
+        ent.fill_(-1.0)
+        ws.fill_(0xAB)
+        dws.fill_(0xCD)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.cpu().numpy().copy() for t in (al, otok, kout, conf, ent, nlen)]
+
+    note(f"[gpu] graph sampled/draft {name}: eager")
+    clear()
+    step(None)
+    want = snapshot()
+    assert (want[0] >= 1).all() and (want[0] <= R).all()
+
+    note(f"[gpu] graph sampled/draft {name}: capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    clear()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(4):
+        clear()                        # eager work between replays, stale workspaces
+        torch.cuda.synchronize()
+        note(f"[gpu] graph sampled/draft {name}: replay {rep}")
         g.replay()
         got = snapshot()
         for i, (x, y) in enumerate(zip(got, want)):
