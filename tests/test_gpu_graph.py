@@ -157,3 +157,89 @@ def test_sampled_acceptance_and_draft_signals_in_a_graph(name):
         got = snapshot()
         for i, (x, y) in enumerate(zip(got, want)):
             assert np.array_equal(x, y), (rep, i)
+
+
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15"])
+def test_tree_step_in_a_graph_replays_like_eager(name):
+    """spec_kv_append -> spec_verify_attn_tree -> spec_accept_tree -> spec_kv_commit_tree
+    captured once; every replay (cache and lengths reset eagerly in between) gives
+    the eager step's outputs, cache bytes and lengths bit for bit."""
+    from workloads import make_tree_plan, tree_tokens_from_target
+    w = MINI[name]
+    fp8 = w.kv_dtype == "fp8_e4m3"
+    ap = make_append_inputs(w)
+    b = ap.base
+    tp = make_tree_plan(w, shape="random", width=3, p_match=0.8)
+    plan = make_accept_plan(w)
+    tok = dev(tree_tokens_from_target(tp, oracle_argmax(plan.logits)))
+    par = dev(tp.parents)
+    tm = torch.from_numpy(np.ascontiguousarray(tp.masks).view(np.int64)).cuda()
+    d = DeviceAttn(b)
+    k0, v0 = d.k.clone(), d.v.clone()
+    ks0 = d.ks.clone() if fp8 else None
+    vs0 = d.vs.clone() if fp8 else None
+    lens0 = dev(ap.committed)
+    lens = lens0.clone()
+    kn, vn = dev(ap.k_new), dev(ap.v_new)
+    lg = dev(plan.logits)
+    B, R, V, D = w.B, w.R, w.V, w.D
+    app = sv.make_append_params(batch=B, num_new=R, num_kv_heads=w.H_kv, head_dim=w.hd,
+                                max_blocks_per_seq=b.block_table.shape[1], num_blocks=b.num_blocks,
+                                kv_dtype=sv.SV_KV_FP8_E4M3 if fp8 else sv.SV_KV_BF16)
+    p = attn_params(b)
+    ws_bytes = sv.spec_verify_attn_workspace_size(p)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty(d.q.shape, dtype=torch.int16, device="cuda")
+    tgt = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    otok = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    aws_bytes = sv.spec_accept_workspace_size(B, D, V)
+    aws = torch.empty(aws_bytes, dtype=torch.uint8, device="cuda")
+
+    def reset():
+        d.k.copy_(k0)
+        d.v.copy_(v0)
+        if fp8:
+            d.ks.copy_(ks0)
+            d.vs.copy_(vs0)
+        lens.copy_(lens0)
+        for t in (out, tgt, al, otok, path):
+            t.fill_(-7)
+
+    def step(stream):
+        sv.spec_kv_append(app, kn, vn, d.k, d.v, d.ks, d.vs, d.bt, lens, lens, stream=stream)
+        sv.spec_verify_attn_tree(p, d.q, d.k, d.v, d.ks, d.vs, d.bt, lens, tm, out, ws, ws_bytes,
+                                 stream=stream)
+        sv.spec_accept_tree(B, D, V, lg, tok, par, tgt, al, otok, path, lens, lens, aws,
+                            aws_bytes, stream=stream)
+        sv.spec_kv_commit_tree(app, kn, vn, d.k, d.v, d.ks, d.vs, d.bt, path, lens, stream=stream)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        ts = [out, tgt, al, otok, path, lens, d.k, d.v] + ([d.ks, d.vs] if fp8 else [])
+        return [t.cpu().numpy().copy() for t in ts]
+
+    note(f"[gpu] graph tree step {name}: eager")
+    reset()
+    step(None)
+    want = snapshot()
+    assert (want[2] >= 1).all() and (want[2] <= R).all()
+
+    note(f"[gpu] graph tree step {name}: capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(4):
+        reset()
+        torch.cuda.synchronize()
+        note(f"[gpu] graph tree step {name}: replay {rep}")
+        g.replay()
+        got = snapshot()
+        for i, (x, y) in enumerate(zip(got, want)):   # bit patterns: spare scales hold NaN
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), (rep, i)
