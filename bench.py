@@ -76,6 +76,13 @@ def attn_algorithmic_flops(inp) -> int:
     return int(inp.kv_lens.astype(np.int64).sum()) * w.H_kv * 4 * w.M * w.hd
 
 
+def attn_exps(inp) -> int:
+    """Exponentials the softmax needs per launch: one per (query row, visible
+    key) pair, M = G*(1+D) rows per (key, KV head) (the causal tail ignored)."""
+    w = inp.w
+    return int(inp.kv_lens.astype(np.int64).sum()) * w.H_kv * w.M
+
+
 def attn_kernel_names(w) -> str:
     """The kernels one spec_verify_attn launch runs for this workload (batches
     up to 2048 take the stream-K path)."""
@@ -103,7 +110,7 @@ def time_append(w, da, stream, sv, calls=20):
     step's own timing.  Not part of the step: the cache of the workload already
     holds those rows."""
     import torch
-    from tests.gpu_util import dev
+    from speculative_decoding_verification_15_amd.device import dev
     from workloads import make_append_inputs
     ap = make_append_inputs(w, base=da.inp)
     kn, vn = dev(ap.k_new), dev(ap.v_new)
@@ -136,7 +143,7 @@ def time_accept_sampled(w, da, stream, sv, calls=20):
     the step's own timing.  The greedy spec_accept is the step's acceptance; this
     is its sampled-decoding counterpart."""
     import torch
-    from tests.gpu_util import dev
+    from speculative_decoding_verification_15_amd.device import dev
     from workloads import make_sampled_accept_inputs
     si = make_sampled_accept_inputs(w)
     B, D, V = w.B, w.D, w.V
@@ -173,7 +180,7 @@ def time_draft_signals(w, stream, sv, calls=20):
     signals and the next draft length (max_draft_len = D, rho = 0.05, G of the
     workload), timed with HIP events after the step's own timing."""
     import torch
-    from tests.gpu_util import dev
+    from speculative_decoding_verification_15_amd.device import dev
     from workloads import make_draft_logits
     z = dev(make_draft_logits(w.B, w.V, seed=w.seed))
     conf = torch.empty((w.B,), dtype=torch.float32, device="cuda")
@@ -207,7 +214,7 @@ def time_tree(w, da, p, ws, ws_bytes, out, stream, sv, calls=20):
     nodes before it), then spec_accept_tree on the first logit set, timed with
     HIP events after the step's own timing."""
     import torch
-    from tests.gpu_util import dev
+    from speculative_decoding_verification_15_amd.device import dev
     from workloads import make_accept_plan, make_tree_plan, tree_tokens_from_target
     tp = make_tree_plan(w, shape="random", width=3, p_match=0.7)
     tm = torch.from_numpy(np.ascontiguousarray(tp.masks).view(np.int64)).cuda()
@@ -250,15 +257,59 @@ def time_tree(w, da, p, ws, ws_bytes, out, stream, sv, calls=20):
             "sum_accept_len": int(al.cpu().sum())}
 
 
+def measure_ceilings(stream, sv):
+    """The machine's own ceilings, measured after the step's timing: a streaming
+    read of 1 GiB (four times the Infinity Cache), a dense bf16 MFMA loop and
+    the vector exp2 rate, each the best of a few launches (HIP events)."""
+    import torch
+    sh = stream.cuda_stream
+
+    def best_us(fn, reps=5):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        fn()                                        # first launch: code load
+        for r in range(reps):
+            ev[2 * r].record(stream)
+            fn()
+            ev[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return min(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps)) * 1e3
+
+    out = {}
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")   # values are never used
+    sink = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+    read = {}
+    for wgs in (1024, 2048, 4096):
+        us = best_us(lambda: sv.sv_ceiling_read(src, nbytes, wgs, sink, stream=sh))
+        read[wgs] = nbytes / (us * 1e-6) / 1e9
+    wgs = max(read, key=read.get)
+    out["read_stream_GBps"] = round(read[wgs], 1)
+    out["read_stream_workgroups"] = wgs
+    del src
+    m_wgs, m_it = 1024, 2048
+    us = best_us(lambda: sv.sv_ceiling_mfma_bf16(m_wgs, m_it, sink, stream=sh))
+    out["mfma_bf16_TFLOPs"] = round(m_wgs * 4 * m_it * 4 * 32768 / (us * 1e-6) / 1e12, 1)
+    e_wgs, e_it = 2048, 512
+    us = best_us(lambda: sv.sv_ceiling_exp2(e_wgs, e_it, sink, stream=sh))
+    out["exp2_per_s"] = float(f"{e_wgs * 256 * e_it * 8 / (us * 1e-6):.4g}")
+    out["method"] = ("sv_ceiling_read (16-byte non-temporal loads, best of 1024/2048/4096 "
+                     "workgroups), sv_ceiling_mfma_bf16 (4 independent 32x32x16 bf16 MFMA chains "
+                     "per wave), sv_ceiling_exp2 (8 independent v_exp_f32 chains per thread); "
+                     "best of 5 launches each, after the timed steps")
+    return out
+
+
 def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
     """Times the oracle (as it is) on whole sequences until ~budget_s of CPU work."""
     from oracle.accept import oracle_accept
     from oracle.attention import oracle_attn
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        blas = None
+    threads = min(affinity, blas) if blas else affinity
     done, tokens, t_total = [], 0, 0.0
     for b in range(w.B):
         t0 = time.perf_counter()
@@ -270,7 +321,8 @@ def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
         done.append(b)
         if t_total >= budget_s:
             break
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads,
+            "affinity_cores": affinity, "blas_threads": blas, "kind": "oracle",
             "sample": f"{len(done)} of {w.B} sequences (all {w.H_kv} KV heads): fp64 attention "
                       f"+ acceptance, {t_total:.1f} s of host time, sum AL = {tokens}",
             "seconds": round(t_total, 2)}
@@ -307,7 +359,7 @@ def main():
         return
 
     import speculative_decoding_verification_15_amd as sv
-    from tests.gpu_util import DeviceAttn, attn_params, dev
+    from speculative_decoding_verification_15_amd.device import DeviceAttn, attn_params, dev
     from workloads import all_workloads, drafts_from_target, make_accept_plan, make_attn_inputs
 
     w = all_workloads()[args.workload]
@@ -317,9 +369,11 @@ def main():
     logits_bytes = w.B * w.R * w.V * 4
     n_sets = int(min(8, max(2, -(-512 * 2 ** 20 // logits_bytes))))
     plan, logit_sets = make_accept_plan(w, n_logit_sets=n_sets)
-    # draft synthesis needs the target token of every row (input preparation)
-    target_host = np.argmax(plan.logits, axis=-1)
-    draft = drafts_from_target(plan, target_host)
+    # Draft synthesis needs the target token of every row (input preparation).
+    # Every rotated logit set gets its own drafts from the same match plan, so
+    # each step sees the configured match probability.
+    drafts = [drafts_from_target(plan, np.argmax(x, axis=-1)) for x in logit_sets]
+    draft = drafts[0]
     t_gen = time.perf_counter() - t_gen
 
     torch.cuda.set_device(0)
@@ -329,7 +383,7 @@ def main():
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty(da.q.shape, dtype=torch.int16, device="cuda")
     lg = [dev(x) for x in logit_sets]
-    dr = dev(draft) if w.D > 0 else None
+    dr = [dev(d) for d in drafts] if w.D > 0 else [None] * n_sets
     B, R, V, D = w.B, w.R, w.V, w.D
     tgt = torch.empty((B, R), dtype=torch.int32, device="cuda")
     al = torch.empty((B,), dtype=torch.int32, device="cuda")
@@ -347,15 +401,14 @@ def main():
                             stream=sh)
         if ev is not None:
             ev[1].record(stream)
-        sv.spec_accept(B, D, V, lg[i % n_sets], dr, tgt, al, otok, da.kl, kv_out, acc_ws,
-                       acc_ws_bytes, stream=sh)
+        sv.spec_accept(B, D, V, lg[i % n_sets], dr[i % n_sets], tgt, al, otok, da.kl, kv_out,
+                       acc_ws, acc_ws_bytes, stream=sh)
         if ev is not None:
             ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    sum_al = [int(al.cpu().sum())]   # AL of the last warm-up step (logit set (W-1) % n)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -372,21 +425,26 @@ def main():
     # acceptance lengths of every logit set in use (the step cycles through them)
     al_per_set = []
     for j in range(n_sets):
-        sv.spec_accept(B, D, V, lg[j], dr, tgt, al, otok, da.kl, kv_out, acc_ws, acc_ws_bytes,
+        sv.spec_accept(B, D, V, lg[j], dr[j], tgt, al, otok, da.kl, kv_out, acc_ws, acc_ws_bytes,
                        stream=sh)
         torch.cuda.synchronize()
         al_per_set.append(int(al.cpu().sum()))
+    # the sets share one match plan, so each gives the same acceptance lengths
+    assert len(set(al_per_set)) == 1, al_per_set
     tokens_timed = sum(al_per_set[i % n_sets] for i in range(args.steps))
 
     append = time_append(w, da, stream, sv)
     sampled = time_accept_sampled(w, da, stream, sv)
     signals = time_draft_signals(w, stream, sv)
     tree = time_tree(w, da, p, ws, ws_bytes, out, stream, sv) if w.B <= 2048 else None
+    ceilings = measure_ceilings(stream, sv)
 
     ms_per_step = total_ms / args.steps
     value = tokens_timed / (total_ms / 1e3)
     attn_us = float(np.mean(t_attn) * 1e3)
     acc_us = float(np.mean(t_acc) * 1e3)
+    attn_steps = t_attn * 1e3
+    last = attn_steps[-min(5, len(attn_steps)):]
     alg_bytes = attn_algorithmic_bytes(inp)
     kv_bytes = attn_algorithmic_kv_bytes(inp)
     achieved = alg_bytes / (attn_us * 1e-6) / 1e9
@@ -422,14 +480,35 @@ def main():
             "kernel": attn_kernel_names(w),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(attn_us, 2)},
+            "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(attn_us, 2),
+            "measured_peak": ceilings["read_stream_GBps"],
+            "frac_of_measured": round(achieved / ceilings["read_stream_GBps"], 4),
+            "median_launch_us": round(float(np.median(attn_steps)), 2),
+            "frac_at_median": round(alg_bytes / (np.median(attn_steps) * 1e-6) / 1e9
+                                    / HBM_PEAK_GBPS, 4)},
+        "attn_us_per_step": {"median": round(float(np.median(attn_steps)), 2),
+                             "min": round(float(attn_steps.min()), 2),
+                             "max": round(float(attn_steps.max()), 2),
+                             "mean_last5": round(float(last.mean()), 2),
+                             "all": [round(float(x), 1) for x in attn_steps]},
+        "step_ms_median": round(float(np.median(t_attn + t_acc)), 4),
         "kv_hbm_GBps": round(kv_gbps, 1),
         "kv_hbm_frac_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                 "measured_peak_tflops": ceilings["mfma_bf16_TFLOPs"],
+                 "frac_of_measured": round(tflops / ceilings["mfma_bf16_TFLOPs"], 4),
                  "algorithmic_flops_per_launch": flops},
+        "softmax_exp2": {"per_launch": attn_exps(inp),
+                         "floor_us_at_measured_rate": round(attn_exps(inp) /
+                                                            ceilings["exp2_per_s"] * 1e6, 1)},
         "accept": {"avg_launch_us": round(acc_us, 2),
-                   "GBps": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9, 1)},
+                   "median_launch_us": round(float(np.median(t_acc) * 1e3), 2),
+                   "GBps": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9, 1),
+                   "frac": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "frac_of_measured": round(B * R * V * 4 / (acc_us * 1e-6) / 1e9
+                                             / ceilings["read_stream_GBps"], 4)},
+        "ceilings": ceilings,
         "append": append,
         "accept_sampled": sampled,
         "draft_signals": signals,

@@ -141,7 +141,9 @@ sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes
  *
  * Size limits (SV_ERR_UNSUPPORTED beyond them): B*R*H_q*hd < 2^31 elements;
  * H_kv*hd*32 < 2^31 (bytes of one physical block of a bf16 cache, all KV
- * heads); num_blocks*H_kv < 2^32 (entries of a scale array).
+ * heads); num_blocks*H_kv < 2^32 (entries of a scale array); for B <= 2048,
+ * B*H_kv*ceil(M/128)*ceil(max_kv_len/32) < 2^31 (32-key tiles of the whole
+ * batch, M = G*R rows per KV head; 256 rows per tile when 128 < M <= 256).
  *
  * Device preconditions: R <= kv_lens[b] <= max_kv_len; block_table[b][j] in
  * [0, num_blocks) for j < ceil(kv_lens[b] / 16).  The other entries of the
@@ -415,8 +417,10 @@ sv_status spec_draft_signals_workspace_size(int32_t rows, int32_t vocab, size_t*
  *   workspace       at least spec_draft_signals_workspace_size() bytes,
  *                   256-byte aligned.
  * Errors: SV_ERR_INVALID for rows outside [1, 65535], vocab < 1, temperature,
- * max_draft_len, rho or group_size out of range, NULL or misaligned pointers;
- * SV_ERR_WORKSPACE.
+ * max_draft_len, rho or group_size out of range, a (group_size, max_draft_len)
+ * pair for which no D in [0, max_draft_len] passes the tile rule (G > 128, not
+ * a multiple of 128, and no multiple of 128 among G (1 + D)), NULL or
+ * misaligned pointers; SV_ERR_WORKSPACE.
  */
 sv_status spec_draft_signals(int32_t rows, int32_t vocab, float temperature,
                              const float* draft_logits, float* confidence, float* entropy,

@@ -22,7 +22,8 @@ EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_w
            "spec_accept", "spec_accept_sampled_workspace_size", "spec_accept_sampled",
            "spec_kv_append", "spec_draft_signals_workspace_size", "spec_draft_signals",
            "spec_verify_attn_tree", "spec_accept_tree", "spec_kv_commit_tree",
-           "sv_status_string", "sv_last_error", "sv_abi_version")
+           "sv_status_string", "sv_last_error", "sv_abi_version",
+           "sv_ceiling_read", "sv_ceiling_mfma_bf16", "sv_ceiling_exp2")
 
 
 class SvAttnParams(ctypes.Structure):
@@ -102,6 +103,12 @@ def _load():
     lib.sv_last_error.restype = ctypes.c_char_p
     lib.sv_abi_version.argtypes = []
     lib.sv_abi_version.restype = I32
+    lib.sv_ceiling_read.argtypes = [P, S, I32, P, P]
+    lib.sv_ceiling_read.restype = U
+    lib.sv_ceiling_mfma_bf16.argtypes = [I32, I32, P, P]
+    lib.sv_ceiling_mfma_bf16.restype = U
+    lib.sv_ceiling_exp2.argtypes = [I32, I32, P, P]
+    lib.sv_ceiling_exp2.restype = U
     return lib
 
 
@@ -129,13 +136,35 @@ def _check(status: int):
         raise SvError(status, last_error())
 
 
-def _ptr(t):
-    """Device address of a tensor (None -> NULL).  Integers pass through."""
+_I32, _F32, _BF16, _U8, _U64 = ("int32",), ("float32",), ("bfloat16", "int16", "uint16"), \
+    ("uint8", "int8", "float8_e4m3fn"), ("int64", "uint64")
+
+
+def _ptr(t, nbytes=None, name="tensor", dtypes=None):
+    """Device address of a tensor (None -> NULL; integers pass through as raw
+    addresses).  A tensor must live on the GPU, be contiguous, have one of the
+    dtypes the header names for the argument and hold at least `nbytes`
+    bytes; otherwise SvError(SV_ERR_INVALID) is raised before any call, since a
+    CPU tensor, a strided view or a short buffer would reach a kernel as a bad
+    address."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not getattr(t, "is_cuda", False):
+        raise SvError(SV_ERR_INVALID, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise SvError(SV_ERR_INVALID, f"{name} must be contiguous")
+    if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+        raise SvError(SV_ERR_INVALID, f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    have = t.numel() * t.element_size()
+    if nbytes is not None and have < nbytes:
+        raise SvError(SV_ERR_INVALID, f"{name} holds {have} bytes; the shape needs {nbytes}")
     return t.data_ptr()
+
+
+def _nbytes(t):
+    return 0 if t is None or isinstance(t, int) else t.numel() * t.element_size()
 
 
 def _stream(stream):
@@ -162,14 +191,35 @@ def spec_verify_attn_workspace_size(params: SvAttnParams) -> int:
     return int(n.value)
 
 
+def _attn_ptrs(p: SvAttnParams, q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, out,
+               workspace, workspace_bytes):
+    """Checked addresses of spec_verify_attn's buffers, sized from the params."""
+    fp8 = p.kv_dtype == SV_KV_FP8_E4M3
+    R = p.draft_len + 1
+    qo = max(p.batch, 0) * R * max(p.num_q_heads, 0) * max(p.head_dim, 0) * 2
+    cache = max(p.num_blocks, 0) * max(p.num_kv_heads, 0) * 16 * max(p.head_dim, 0) * (1 if fp8 else 2)
+    scales = max(p.num_blocks, 0) * max(p.num_kv_heads, 0) * 4
+    cdt = _U8 if fp8 else _BF16
+    return (_ptr(q, qo, "q", _BF16), _ptr(k_cache, cache, "k_cache", cdt),
+            _ptr(v_cache, cache, "v_cache", cdt), _ptr(k_scale, scales, "k_scale", _F32),
+            _ptr(v_scale, scales, "v_scale", _F32),
+            _ptr(block_table, max(p.batch, 0) * max(p.max_blocks_per_seq, 0) * 4, "block_table", _I32),
+            _ptr(kv_lens, max(p.batch, 0) * 4, "kv_lens", _I32), _ptr(out, qo, "out", _BF16),
+            _ptr(workspace, workspace_bytes, "workspace"))
+
+
+def _ws_bytes(workspace, workspace_bytes):
+    return _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+
+
 def spec_verify_attn(params: SvAttnParams, q, k_cache, v_cache, k_scale, v_scale, block_table,
                      kv_lens, out, workspace=None, workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
-            workspace.numel() * workspace.element_size()
-    _check(_lib.spec_verify_attn(ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(kv_lens),
-                                 _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    pq, pk, pv, pks, pvs, pbt, pkl, pout, pws = _attn_ptrs(
+        params, q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, out, workspace,
+        workspace_bytes)
+    _check(_lib.spec_verify_attn(ctypes.byref(params), pq, pk, pv, pks, pvs, pbt, pkl, pout, pws,
+                                 workspace_bytes, _stream(stream)))
 
 
 def spec_accept_workspace_size(batch: int, draft_len: int, vocab: int) -> int:
@@ -178,14 +228,24 @@ def spec_accept_workspace_size(batch: int, draft_len: int, vocab: int) -> int:
     return int(n.value)
 
 
+def _rows(batch, draft_len):
+    return max(batch, 0) * (max(draft_len, 0) + 1)
+
+
 def spec_accept(batch, draft_len, vocab, logits, draft, target_tokens, accept_len, out_tokens,
                 kv_lens_in, kv_lens_out, workspace, workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
-            workspace.numel() * workspace.element_size()
-    _check(_lib.spec_accept(batch, draft_len, vocab, _ptr(logits), _ptr(draft), _ptr(target_tokens),
-                            _ptr(accept_len), _ptr(out_tokens), _ptr(kv_lens_in), _ptr(kv_lens_out),
-                            _ptr(workspace), workspace_bytes, _stream(stream)))
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    B, rows = max(batch, 0), _rows(batch, draft_len)
+    _check(_lib.spec_accept(batch, draft_len, vocab,
+                            _ptr(logits, rows * max(vocab, 0) * 4, "logits", _F32),
+                            _ptr(draft, B * max(draft_len, 0) * 4, "draft", _I32),
+                            _ptr(target_tokens, rows * 4, "target_tokens", _I32),
+                            _ptr(accept_len, B * 4, "accept_len", _I32),
+                            _ptr(out_tokens, rows * 4, "out_tokens", _I32),
+                            _ptr(kv_lens_in, B * 4, "kv_lens_in", _I32),
+                            _ptr(kv_lens_out, B * 4, "kv_lens_out", _I32),
+                            _ptr(workspace, workspace_bytes, "workspace"), workspace_bytes,
+                            _stream(stream)))
 
 
 def spec_accept_sampled_workspace_size(batch: int, draft_len: int, vocab: int) -> int:
@@ -197,14 +257,20 @@ def spec_accept_sampled_workspace_size(batch: int, draft_len: int, vocab: int) -
 def spec_accept_sampled(batch, draft_len, vocab, temperature, target_logits, draft_logits, draft,
                         u_accept, u_sample, accept_len, out_tokens, kv_lens_in, kv_lens_out,
                         workspace, workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
-            workspace.numel() * workspace.element_size()
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    B, rows, D, V = max(batch, 0), _rows(batch, draft_len), max(draft_len, 0), max(vocab, 0)
     _check(_lib.spec_accept_sampled(batch, draft_len, vocab, float(temperature),
-                                    _ptr(target_logits), _ptr(draft_logits), _ptr(draft),
-                                    _ptr(u_accept), _ptr(u_sample), _ptr(accept_len),
-                                    _ptr(out_tokens), _ptr(kv_lens_in), _ptr(kv_lens_out),
-                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+                                    _ptr(target_logits, rows * V * 4, "target_logits", _F32),
+                                    _ptr(draft_logits, B * D * V * 4, "draft_logits", _F32),
+                                    _ptr(draft, B * D * 4, "draft", _I32),
+                                    _ptr(u_accept, B * D * 4, "u_accept", _F32),
+                                    _ptr(u_sample, B * 4, "u_sample", _F32),
+                                    _ptr(accept_len, B * 4, "accept_len", _I32),
+                                    _ptr(out_tokens, rows * 4, "out_tokens", _I32),
+                                    _ptr(kv_lens_in, B * 4, "kv_lens_in", _I32),
+                                    _ptr(kv_lens_out, B * 4, "kv_lens_out", _I32),
+                                    _ptr(workspace, workspace_bytes, "workspace"), workspace_bytes,
+                                    _stream(stream)))
 
 
 
@@ -214,11 +280,28 @@ def make_append_params(*, batch, num_new, num_kv_heads, head_dim, max_blocks_per
                           num_blocks, kv_dtype)
 
 
+def _append_ptrs(p: SvAppendParams, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table):
+    """Checked addresses of the buffers spec_kv_append and spec_kv_commit_tree share."""
+    fp8 = p.kv_dtype == SV_KV_FP8_E4M3
+    rows = max(p.batch, 0) * max(p.num_new, 0) * max(p.num_kv_heads, 0) * max(p.head_dim, 0) * 2
+    cache = max(p.num_blocks, 0) * max(p.num_kv_heads, 0) * 16 * max(p.head_dim, 0) * (1 if fp8 else 2)
+    scales = max(p.num_blocks, 0) * max(p.num_kv_heads, 0) * 4
+    cdt = _U8 if fp8 else _BF16
+    return (_ptr(k_new, rows, "k_new", _BF16), _ptr(v_new, rows, "v_new", _BF16),
+            _ptr(k_cache, cache, "k_cache", cdt), _ptr(v_cache, cache, "v_cache", cdt),
+            _ptr(k_scale, scales, "k_scale", _F32), _ptr(v_scale, scales, "v_scale", _F32),
+            _ptr(block_table, max(p.batch, 0) * max(p.max_blocks_per_seq, 0) * 4, "block_table",
+                 _I32))
+
+
 def spec_kv_append(params: SvAppendParams, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
                    block_table, kv_lens_in, kv_lens_out, stream=None) -> None:
-    _check(_lib.spec_kv_append(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
-                               _ptr(kv_lens_in), _ptr(kv_lens_out), _stream(stream)))
+    B = max(params.batch, 0)
+    _check(_lib.spec_kv_append(ctypes.byref(params),
+                               *_append_ptrs(params, k_new, v_new, k_cache, v_cache, k_scale,
+                                             v_scale, block_table),
+                               _ptr(kv_lens_in, B * 4, "kv_lens_in", _I32),
+                               _ptr(kv_lens_out, B * 4, "kv_lens_out", _I32), _stream(stream)))
 
 
 def spec_draft_signals_workspace_size(rows: int, vocab: int) -> int:
@@ -230,43 +313,70 @@ def spec_draft_signals_workspace_size(rows: int, vocab: int) -> int:
 def spec_draft_signals(rows, vocab, temperature, draft_logits, confidence, entropy, next_draft_len,
                        max_draft_len, rho, group_size, workspace, workspace_bytes=None,
                        stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
-            workspace.numel() * workspace.element_size()
-    _check(_lib.spec_draft_signals(rows, vocab, float(temperature), _ptr(draft_logits),
-                                   _ptr(confidence), _ptr(entropy), _ptr(next_draft_len),
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    n = max(rows, 0)
+    _check(_lib.spec_draft_signals(rows, vocab, float(temperature),
+                                   _ptr(draft_logits, n * max(vocab, 0) * 4, "draft_logits", _F32),
+                                   _ptr(confidence, n * 4, "confidence", _F32),
+                                   _ptr(entropy, n * 4, "entropy", _F32),
+                                   _ptr(next_draft_len, n * 4, "next_draft_len", _I32),
                                    int(max_draft_len), float(rho), int(group_size),
-                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+                                   _ptr(workspace, workspace_bytes, "workspace"), workspace_bytes,
+                                   _stream(stream)))
 
 
 def spec_verify_attn_tree(params: SvAttnParams, q, k_cache, v_cache, k_scale, v_scale,
                           block_table, kv_lens, tree_mask, out, workspace=None,
                           workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
-            workspace.numel() * workspace.element_size()
-    _check(_lib.spec_verify_attn_tree(ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                      _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
-                                      _ptr(kv_lens), _ptr(tree_mask), _ptr(out), _ptr(workspace),
-                                      workspace_bytes, _stream(stream)))
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    pq, pk, pv, pks, pvs, pbt, pkl, pout, pws = _attn_ptrs(
+        params, q, k_cache, v_cache, k_scale, v_scale, block_table, kv_lens, out, workspace,
+        workspace_bytes)
+    ptm = _ptr(tree_mask, _rows(params.batch, params.draft_len) * 8, "tree_mask", _U64)
+    _check(_lib.spec_verify_attn_tree(ctypes.byref(params), pq, pk, pv, pks, pvs, pbt, pkl, ptm,
+                                      pout, pws, workspace_bytes, _stream(stream)))
 
 
 def spec_accept_tree(batch, draft_len, vocab, logits, tokens, parents, target_tokens, accept_len,
                      out_tokens, accept_path, kv_lens_in, kv_lens_out, workspace,
                      workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
-            workspace.numel() * workspace.element_size()
-    _check(_lib.spec_accept_tree(batch, draft_len, vocab, _ptr(logits), _ptr(tokens),
-                                 _ptr(parents), _ptr(target_tokens), _ptr(accept_len),
-                                 _ptr(out_tokens), _ptr(accept_path), _ptr(kv_lens_in),
-                                 _ptr(kv_lens_out), _ptr(workspace), workspace_bytes,
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    B, rows = max(batch, 0), _rows(batch, draft_len)
+    _check(_lib.spec_accept_tree(batch, draft_len, vocab,
+                                 _ptr(logits, rows * max(vocab, 0) * 4, "logits", _F32),
+                                 _ptr(tokens, rows * 4, "tokens", _I32),
+                                 _ptr(parents, rows * 4, "parents", _I32),
+                                 _ptr(target_tokens, rows * 4, "target_tokens", _I32),
+                                 _ptr(accept_len, B * 4, "accept_len", _I32),
+                                 _ptr(out_tokens, rows * 4, "out_tokens", _I32),
+                                 _ptr(accept_path, rows * 4, "accept_path", _I32),
+                                 _ptr(kv_lens_in, B * 4, "kv_lens_in", _I32),
+                                 _ptr(kv_lens_out, B * 4, "kv_lens_out", _I32),
+                                 _ptr(workspace, workspace_bytes, "workspace"), workspace_bytes,
                                  _stream(stream)))
 
 
 def spec_kv_commit_tree(params: SvAppendParams, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
                         block_table, accept_path, kv_lens, stream=None) -> None:
-    _check(_lib.spec_kv_commit_tree(ctypes.byref(params), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-                                    _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-                                    _ptr(block_table), _ptr(accept_path), _ptr(kv_lens),
-                                    _stream(stream)))
+    B = max(params.batch, 0)
+    _check(_lib.spec_kv_commit_tree(ctypes.byref(params),
+                                    *_append_ptrs(params, k_new, v_new, k_cache, v_cache, k_scale,
+                                                  v_scale, block_table),
+                                    _ptr(accept_path, B * max(params.num_new, 0) * 4,
+                                         "accept_path", _I32),
+                                    _ptr(kv_lens, B * 4, "kv_lens", _I32), _stream(stream)))
+
+
+def sv_ceiling_read(src, nbytes, workgroups, sink, stream=None) -> None:
+    _check(_lib.sv_ceiling_read(_ptr(src, nbytes, "src"), nbytes, int(workgroups),
+                                _ptr(sink, int(workgroups) * 4, "sink", _F32), _stream(stream)))
+
+
+def sv_ceiling_mfma_bf16(workgroups, iters, sink, stream=None) -> None:
+    _check(_lib.sv_ceiling_mfma_bf16(int(workgroups), int(iters),
+                                     _ptr(sink, int(workgroups) * 16, "sink", _F32), _stream(stream)))
+
+
+def sv_ceiling_exp2(workgroups, iters, sink, stream=None) -> None:
+    _check(_lib.sv_ceiling_exp2(int(workgroups), int(iters),
+                                _ptr(sink, int(workgroups) * 1024, "sink", _F32), _stream(stream)))

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libspecverify.so")
 SOURCES = ("sv_api.cpp", "sv_attn.hip", "sv_accept.hip", "sv_sample.hip", "sv_append.hip",
-           "sv_draft.hip")
+           "sv_draft.hip", "sv_ceil.hip")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code.  MFMA accumulators

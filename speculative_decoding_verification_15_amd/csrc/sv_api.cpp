@@ -3,6 +3,7 @@
 // runs before the first HIP call, so invalid calls return an error without
 // touching the device.
 #include "spec_verify.h"
+#include "sv_ceilings.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -85,6 +86,14 @@ sv_status make_attn_plan(const sv_attn_params* p, sv::AttnPlan& plan) {
     return fail(SV_ERR_UNSUPPORTED, "too many workgroups for one launch");
   const long long ws_rows = (long long)plan.B * plan.H_kv * plan.s_max * plan.M;
   if (ws_rows >= (1LL << 31)) return fail(SV_ERR_UNSUPPORTED, "split workspace too large");
+  if (plan.streamk) {
+    // the stream-K work list counts 32-key tiles of every unit in int32
+    const long long tiles = (long long)plan.B * plan.H_kv * plan.m_tiles *
+                            ((plan.max_kv_len + 31LL) / 32);
+    if (tiles >= (1LL << 31))
+      return fail(SV_ERR_UNSUPPORTED, "%lld key tiles in one call (batch * num_kv_heads * row tiles "
+                  "* ceil(max_kv_len / 32)) exceed the 2^31 the work list can count", tiles);
+  }
   return SV_OK;
 }
 
@@ -370,6 +379,17 @@ static sv_status check_draft_signals(int32_t rows, int32_t vocab, float temperat
   if (!(rho >= 0.f) || !std::isfinite(rho)) return fail(SV_ERR_INVALID, "rho must be finite and >= 0");
   if (group_size < 0 || group_size > 1024)
     return fail(SV_ERR_INVALID, "group_size must be in [0, 1024] (got %d)", group_size);
+  if (group_size > 0) {
+    // the tile rule must leave at least one draft length to choose from
+    bool any = false;
+    for (int d = 0; d <= max_draft_len && !any; ++d) {
+      const int rows = group_size * (d + 1);
+      any = rows <= 128 || rows % 128 == 0;
+    }
+    if (!any)
+      return fail(SV_ERR_INVALID, "no draft length in [0, %d] passes the tile rule for group_size "
+                  "%d (G (1 + D) <= 128 or a multiple of 128)", max_draft_len, group_size);
+  }
   return SV_OK;
 }
 
@@ -402,6 +422,46 @@ sv_status spec_draft_signals(int32_t rows, int32_t vocab, float temperature,
   hipError_t e = sv::launch_draft_signals(rows, vocab, temperature, draft_logits, confidence,
                                           entropy, next_draft_len, max_draft_len, rho, group_size,
                                           workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+static sv_status check_ceiling_grid(int32_t workgroups, int32_t iters, const float* sink) {
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(SV_ERR_INVALID, "workgroups must be in [1, 65536] (got %d)", workgroups);
+  if (iters < 1 || iters > (1 << 20))
+    return fail(SV_ERR_INVALID, "iters must be in [1, 2^20] (got %d)", iters);
+  if (!sink || !aligned(sink, 4)) return fail(SV_ERR_INVALID, "sink must be a 4-byte aligned pointer");
+  return SV_OK;
+}
+
+sv_status sv_ceiling_read(const void* src, size_t bytes, int32_t workgroups, float* sink,
+                          void* stream) {
+  sv_status s = check_ceiling_grid(workgroups, 1, sink);
+  if (s != SV_OK) return s;
+  if (!src || !aligned(src, 16)) return fail(SV_ERR_INVALID, "src must be a 16-byte aligned pointer");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(SV_ERR_INVALID, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  hipError_t e = sv::launch_ceiling_read(src, bytes, workgroups, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+sv_status sv_ceiling_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  sv_status s = check_ceiling_grid(workgroups, iters, sink);
+  if (s != SV_OK) return s;
+  hipError_t e = sv::launch_ceiling_mfma(workgroups, iters, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
+sv_status sv_ceiling_exp2(int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  sv_status s = check_ceiling_grid(workgroups, iters, sink);
+  if (s != SV_OK) return s;
+  hipError_t e = sv::launch_ceiling_exp2(workgroups, iters, sink, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return SV_OK;

@@ -62,4 +62,10 @@ hipError_t launch_kv_append(const AppendPlan& plan, const void* k_new, const voi
                             const int32_t* table, const int32_t* kv_in, int32_t* kv_out,
                             const int32_t* path, hipStream_t stream);
 
+// Machine ceilings (sv_ceil.hip, C header sv_ceilings.h).
+hipError_t launch_ceiling_read(const void* src, size_t bytes, int wgs, float* sink,
+                               hipStream_t stream);
+hipError_t launch_ceiling_mfma(int wgs, int iters, float* sink, hipStream_t stream);
+hipError_t launch_ceiling_exp2(int wgs, int iters, float* sink, hipStream_t stream);
+
 }  // namespace sv
