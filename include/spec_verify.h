@@ -211,12 +211,34 @@ sv_status spec_accept_workspace_size(int32_t batch, int32_t draft_len, int32_t v
  *   kv_lens_in     [B] int32, read.
  *   kv_lens_out    [B] int32, written; may be the same pointer as kv_lens_in
  *                  (in-place commit).
- *   workspace      at least spec_accept_workspace_size() bytes, 256-byte aligned.
+ *   workspace      at least spec_accept_workspace_size() bytes, 256-byte aligned;
+ *                  contents on entry are ignored.
  */
 sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
                       const int32_t* draft, int32_t* target_tokens, int32_t* accept_len,
                       int32_t* out_tokens, const int32_t* kv_lens_in, int32_t* kv_lens_out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_accept without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments (minus the workspace), results and
+ * errors as spec_accept, same kernels.  The per-chunk results live in a fixed
+ * device array of the library instead of a workspace: 4 MiB on each GPU it
+ * runs on, held until the process ends, its address looked up once per device
+ * on the first call there.  The call allocates nothing and calls no allocating
+ * routine; every call overwrites the entries it reads, so nothing is cleared
+ * between calls.  Every call on a GPU uses that GPU's one array: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and give
+ * unspecified results.
+ * Limit: batch * (1 + draft_len) * ceil(vocab / 4096) * 8 bytes <= 4 MiB
+ * (e.g. 512 rows of a 128256-token vocabulary use 128 KiB); SV_ERR_UNSUPPORTED
+ * beyond it.
+ */
+sv_status spec_accept_noalloc(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
+                              const int32_t* draft, int32_t* target_tokens, int32_t* accept_len,
+                              int32_t* out_tokens, const int32_t* kv_lens_in,
+                              int32_t* kv_lens_out, void* stream);
 
 /*
  * Greedy acceptance over a draft tree (the nodes scored by spec_verify_attn_tree).

@@ -7,7 +7,7 @@ binding: the functions carry the C names and only marshal arguments.
 from ._lib import (EXPORTS, LIB_PATH, SV_ERR_INVALID, SV_ERR_LAUNCH, SV_ERR_UNSUPPORTED,
                    SV_ERR_WORKSPACE, SV_KV_BF16, SV_KV_FP8_E4M3, SV_OK, SvAppendParams,
                    SvAttnParams, SvError, abi_version, last_error, library, make_append_params,
-                   make_attn_params, spec_accept, spec_kv_append, spec_draft_signals,
+                   make_attn_params, spec_accept, spec_accept_noalloc, spec_kv_append, spec_draft_signals,
                    spec_draft_signals_workspace_size, spec_verify_attn_tree, spec_accept_tree,
                    spec_kv_commit_tree,
                    spec_accept_sampled, spec_accept_sampled_workspace_size,
@@ -18,7 +18,7 @@ __all__ = [
     "EXPORTS", "LIB_PATH", "SV_OK", "SV_ERR_INVALID", "SV_ERR_WORKSPACE", "SV_ERR_UNSUPPORTED",
     "SV_ERR_LAUNCH", "SV_KV_BF16", "SV_KV_FP8_E4M3", "SvAppendParams", "SvAttnParams", "SvError",
     "abi_version", "last_error", "library", "make_append_params", "make_attn_params",
-    "spec_accept", "spec_accept_sampled", "spec_kv_append", "spec_draft_signals",
+    "spec_accept", "spec_accept_noalloc", "spec_accept_sampled", "spec_kv_append", "spec_draft_signals",
     "spec_draft_signals_workspace_size", "spec_verify_attn_tree", "spec_accept_tree",
     "spec_kv_commit_tree",
     "spec_accept_sampled_workspace_size", "spec_accept_workspace_size",

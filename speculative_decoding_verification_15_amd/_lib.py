@@ -23,7 +23,7 @@ EXPORTS = ("spec_verify_attn_workspace_size", "spec_verify_attn", "spec_accept_w
            "spec_kv_append", "spec_draft_signals_workspace_size", "spec_draft_signals",
            "spec_verify_attn_tree", "spec_accept_tree", "spec_kv_commit_tree",
            "sv_status_string", "sv_last_error", "sv_abi_version",
-           "sv_ceiling_read", "sv_ceiling_mfma_bf16", "sv_ceiling_exp2")
+           "sv_ceiling_read", "sv_ceiling_mfma_bf16", "sv_ceiling_exp2", "spec_accept_noalloc")
 
 
 class SvAttnParams(ctypes.Structure):
@@ -80,6 +80,8 @@ def _load():
     lib.spec_accept_workspace_size.restype = U
     lib.spec_accept.argtypes = [I32, I32, I32] + [P] * 8 + [S, P]
     lib.spec_accept.restype = U
+    lib.spec_accept_noalloc.argtypes = [I32, I32, I32] + [P] * 8
+    lib.spec_accept_noalloc.restype = U
     lib.spec_accept_sampled_workspace_size.argtypes = [I32, I32, I32, ctypes.POINTER(S)]
     lib.spec_accept_sampled_workspace_size.restype = U
     lib.spec_accept_sampled.argtypes = [I32, I32, I32, ctypes.c_float] + [P] * 10 + [S, P]
@@ -246,6 +248,19 @@ def spec_accept(batch, draft_len, vocab, logits, draft, target_tokens, accept_le
                             _ptr(kv_lens_out, B * 4, "kv_lens_out", _I32),
                             _ptr(workspace, workspace_bytes, "workspace"), workspace_bytes,
                             _stream(stream)))
+
+
+def spec_accept_noalloc(batch, draft_len, vocab, logits, draft, target_tokens, accept_len,
+                        out_tokens, kv_lens_in, kv_lens_out, stream=None) -> None:
+    B, rows = max(batch, 0), _rows(batch, draft_len)
+    _check(_lib.spec_accept_noalloc(batch, draft_len, vocab,
+                                    _ptr(logits, rows * max(vocab, 0) * 4, "logits", _F32),
+                                    _ptr(draft, B * max(draft_len, 0) * 4, "draft", _I32),
+                                    _ptr(target_tokens, rows * 4, "target_tokens", _I32),
+                                    _ptr(accept_len, B * 4, "accept_len", _I32),
+                                    _ptr(out_tokens, rows * 4, "out_tokens", _I32),
+                                    _ptr(kv_lens_in, B * 4, "kv_lens_in", _I32),
+                                    _ptr(kv_lens_out, B * 4, "kv_lens_out", _I32), _stream(stream)))
 
 
 def spec_accept_sampled_workspace_size(batch: int, draft_len: int, vocab: int) -> int:

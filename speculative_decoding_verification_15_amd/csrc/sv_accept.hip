@@ -16,6 +16,8 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 
+#include <mutex>
+
 namespace sv {
 
 struct ArgmaxPart {
@@ -233,6 +235,40 @@ hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t
   sv_accept_finalize<<<B, kWave, 0, stream>>>(part, chunks, D, draft, target, accept_len,
                                                out_tokens, kv_in, kv_out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance without a workspace argument (spec_accept_noalloc): the chunk
+// results live in this fixed device array instead of a caller's workspace.
+// Each GPU the library runs on holds its own copy until the process ends.  Its
+// address on a device comes from hipGetSymbolAddress (in host code the array's
+// name is only a stand-in, never a device address), taken once per device with
+// that device current and kept.  Every call overwrites the entries it reads
+// before reading them, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kAcceptScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t accept_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 }  // namespace sv

@@ -215,6 +215,36 @@ sv_status spec_accept(int32_t batch, int32_t draft_len, int32_t vocab, const flo
   return SV_OK;
 }
 
+sv_status spec_accept_noalloc(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
+                              const int32_t* draft, int32_t* target_tokens, int32_t* accept_len,
+                              int32_t* out_tokens, const int32_t* kv_lens_in,
+                              int32_t* kv_lens_out, void* stream) {
+  sv_status s = check_accept_shape(batch, draft_len, vocab);
+  if (s != SV_OK) return s;
+  if (!logits || !target_tokens || !accept_len || !out_tokens || !kv_lens_in || !kv_lens_out)
+    return fail(SV_ERR_INVALID, "a required pointer is NULL");
+  if (draft_len > 0 && !draft) return fail(SV_ERR_INVALID, "draft is NULL with draft_len > 0");
+  if (!aligned(logits, 16)) return fail(SV_ERR_INVALID, "logits must be 16-byte aligned");
+  if (!aligned(target_tokens, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
+      !aligned(kv_lens_in, 4) || !aligned(kv_lens_out, 4) || (draft && !aligned(draft, 4)))
+    return fail(SV_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  const size_t need = sv::accept_workspace_bytes(batch, draft_len, vocab);
+  if (need > sv::kAcceptScratchBytes)
+    return fail(SV_ERR_UNSUPPORTED, "batch %d, draft_len %d, vocab %d need %zu bytes of scratch "
+                "(8 per 4096-logit chunk of every row); the fixed array holds %zu", batch,
+                draft_len, vocab, need, sv::kAcceptScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = sv::accept_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(SV_ERR_LAUNCH, "scratch set-up failed: %s", hipGetErrorString(e));
+  e = sv::launch_accept(batch, draft_len, vocab, logits, draft, target_tokens, accept_len,
+                        out_tokens, kv_lens_in, kv_lens_out, scratch,
+                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return SV_OK;
+}
+
 sv_status spec_accept_tree(int32_t batch, int32_t draft_len, int32_t vocab, const float* logits,
                            const int32_t* tokens, const int32_t* parents, int32_t* target_tokens,
                            int32_t* accept_len, int32_t* out_tokens, int32_t* accept_path,

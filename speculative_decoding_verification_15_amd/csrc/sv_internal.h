@@ -20,6 +20,11 @@ inline size_t accept_workspace_bytes(int B, int D, int V) {
   return (size_t)B * (size_t)(D + 1) * (size_t)argmax_chunks(V) * 8u;
 }
 
+// spec_accept_noalloc: the library's fixed device array for the chunk results
+// (4 MiB per device); `ptr` receives this device's address of it.
+constexpr size_t kAcceptScratchBytes = 4u << 20;
+hipError_t accept_scratch(void** ptr);
+
 hipError_t launch_accept(int B, int D, int V, const float* logits, const int32_t* draft,
                          int32_t* target, int32_t* accept_len, int32_t* out_tokens,
                          const int32_t* kv_in, int32_t* kv_out, void* ws, hipStream_t stream);

@@ -551,3 +551,26 @@ def test_streamk_tile_count_overflow_is_rejected():
     assert "tiles" in sv.last_error()
     kw["max_kv_len"] = 524288 - 32
     assert sv.spec_verify_attn_workspace_size(sv.make_attn_params(**kw)) > 0
+
+
+def test_accept_noalloc_argument_errors():
+    """spec_accept_noalloc checks like spec_accept, and refuses shapes whose chunk
+    results would not fit its fixed 4 MiB array, all before any launch."""
+    lib = sv.library()
+    B, D, V = 4, 3, 1000
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+
+    def call(i=None, val=None, B=B, D=D, V=V):
+        a = list(base)
+        if i is not None:
+            a[i] = val
+        return lib.spec_accept_noalloc(B, D, V, *a, None)
+    for i in range(7):
+        assert call(i, None) == sv.SV_ERR_INVALID, i
+    assert call(0, FAKE + 4) == sv.SV_ERR_INVALID
+    assert call(2, FAKE + 2) == sv.SV_ERR_INVALID
+    assert call(B=0) == sv.SV_ERR_INVALID
+    assert call(D=64) == sv.SV_ERR_INVALID
+    # 1024 x 16 rows of 33 chunks: 4.3 MB of chunk results > 4 MiB
+    assert call(B=1024, D=15, V=128256 + 4096) == sv.SV_ERR_UNSUPPORTED
+    assert "4194304" in sv.last_error()
