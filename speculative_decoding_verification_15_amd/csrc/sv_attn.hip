@@ -324,42 +324,6 @@ __device__ __forceinline__ bool softmax_sub_sk(const f32x16& x, float c, float& 
   return __ballot(move) != 0;
 }
 
-// softmax_sub for a tile decoded from e4m3 codes: the scores of key block b
-// (16 keys: registers 8b .. 8b + 7) are scaled by cb = c * (K mantissa of
-// block b), and the probabilities of block b are returned times the block's V
-// mantissa mvb (as the PV product needs them), while l accumulates the
-// probabilities themselves.
-__device__ __forceinline__ bool softmax_sub_fp8(const f32x16& x, float c0, float c1, float mv0,
-                                                float mv1, float& m_ref, float& l_run,
-                                                float& alpha, bf16x8& p0, bf16x8& p1) {
-  float h0 = x[0], h1 = x[8];
-#pragma unroll
-  for (int v = 1; v < 8; ++v) {
-    h0 = fmaximum(h0, x[v]);
-    h1 = fmaximum(h1, x[8 + v]);
-  }
-  const float tmax = halves_maximum(fmaximum(h0 * c0, h1 * c1));
-  const bool move = tmax > m_ref + kLazyRescale;   // the running maximum starts at kNoMax
-  alpha = move ? fast_exp2(m_ref - tmax) : 1.f;
-  m_ref = move ? tmax : m_ref;
-  const float m_neg = -m_ref;
-  const float a0 = m_neg + __builtin_amdgcn_logf(mv0), a1 = m_neg + __builtin_amdgcn_logf(mv1);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p0[j] = (__bf16)fast_exp2(__builtin_fmaf(x[j], c0, a0));
-    p1[j] = (__bf16)fast_exp2(__builtin_fmaf(x[8 + j], c1, a1));
-  }
-  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[j], p0[j + 1]}, one, s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[j], p1[j + 1]}, one, s1, false);
-  }
-  l_run = l_run * alpha + s0 * __builtin_amdgcn_rcpf(mv0) + s1 * __builtin_amdgcn_rcpf(mv1);
-  return __ballot(move) != 0;
-}
-
 // Online-softmax update plus the O rescale in place (used by the direct kernel).
 template <int DB, bool MASKED>
 __device__ __forceinline__ void softmax_tile(f32x16 (&x)[2], const float (&cs)[2][2],
@@ -934,7 +898,8 @@ struct SkTile {
   static constexpr int kStages8 = 2 * SV_STREAM_RING_BYTES / kStage;   // one 8-wave workgroup per CU
 };
 
-// pref[b] = tiles of all units of sequences before b, for b = 0 .. B.
+// pref[b] = tiles of KEYS keys of all units of sequences before b, for b = 0 .. B.
+template <int KEYS>
 __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* wsum) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
@@ -944,7 +909,7 @@ __device__ __forceinline__ void build_prefix(const AttnArgs& a, int* pref, int* 
   const int lo = min(tid * chunk, a.B), hi = min(lo + chunk, a.B);
   int sum = 0;
   for (int b = lo; b < hi; ++b) {
-    sum += ((clamp_len(a, b) + kSkKeys - 1) / kSkKeys) * per_seq;
+    sum += ((clamp_len(a, b) + KEYS - 1) / KEYS) * per_seq;
     pref[b + 1] = sum;                      // inclusive within this thread's chunk
   }
   // exclusive scan of the per-thread sums: within each wave, then across waves
@@ -996,13 +961,15 @@ __device__ __forceinline__ Cursor cursor_at(const AttnArgs& a, const int* pref, 
 }
 
 // Tiles of each unit of sequence b (the per-sequence count build_prefix sums).
+template <int KEYS>
 __device__ __forceinline__ int unit_tiles(const AttnArgs& a, int b) {
-  return (clamp_len_s(a, b) + kSkKeys - 1) / kSkKeys;
+  return (clamp_len_s(a, b) + KEYS - 1) / KEYS;
 }
 
 // Advances to the next tile of the work list.  The tile count of a new
 // sequence comes from kv_lens (a scalar load, once per sequence), so the
 // prefix table is needed only to place a range's first tile.
+template <int KEYS>
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   if (++c.tile < c.T) return;
   c.tile = 0;
@@ -1012,7 +979,7 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c) {
   c.kvh = 0;
   do {
     ++c.b;
-  } while (c.b < a.B && (c.T = unit_tiles(a, c.b)) == 0);
+  } while (c.b < a.B && (c.T = unit_tiles<KEYS>(a, c.b)) == 0);
   c.row = a.block_table + (size_t)c.b * a.max_blocks;
 }
 
@@ -1188,7 +1155,7 @@ void sv_attn_streamk(AttnArgs a) {
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_wsum = s_pref + kStreamMaxBatch + 1;
 
-  build_prefix(a, s_pref, s_wsum);
+  build_prefix<kSkKeys>(a, s_pref, s_wsum);
   const int W = uniform(s_pref[a.B]);
   const int Wp = max((W + (int)gridDim.x - 1) / (int)gridDim.x, a.min_tiles);
   const int tid = threadIdx.x;
@@ -1268,7 +1235,7 @@ void sv_attn_streamk(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {         // past the range: the last tile again
     issue(ci, ent, k);
-    if (gi + 1 < g1) cursor_next(a, ci);
+    if (gi + 1 < g1) cursor_next<kSkKeys>(a, ci);
     ++gi;
     ent = entry(ci);
   }
@@ -1306,12 +1273,12 @@ void sv_attn_streamk(AttnArgs a) {
     // nothing issued later.
     if (g + 1 < g1 && cc.tile + 1 == cc.T) {
       Cursor cn = cc;
-      cursor_next(a, cn);
+      cursor_next<kSkKeys>(a, cn);
       active_n = seg_ctx(cn, rn);
       if (active_n) load_q_raw<HD>(a, rn, qn);
     }
     issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
-    if (gi + 1 < g1) cursor_next(a, ci);
+    if (gi + 1 < g1) cursor_next<kSkKeys>(a, ci);
     ++gi;
     ent = entry(ci);
 
@@ -1360,50 +1327,321 @@ void sv_attn_streamk(AttnArgs a) {
                            cc.tile == cc.T - 1 && seg_start == g - cc.tile,
                            (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
-    if (g + 1 < g1) cursor_next(a, cc);
+    if (g + 1 < g1) cursor_next<kSkKeys>(a, cc);
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
 
-// Stream-K kernel for e4m3 caches.  The same work list, ranges, segments and
-// merge as the bf16 kernel; what differs is the tile supply.  A 16-key block
-// of e4m3 K or V is hd x 16 codes (half the bf16 bytes): the codes of NS8
-// tiles stream through a DMA ring, and at every tile each wave decodes the
-// block it moved for the next tile -- codes times the block's scale, rounded
-// once to bf16 -- into one of two bf16 images laid out like a bf16 ring
-// stage (V past the end of the sequence zeroed), on which the tile is then
-// computed exactly as in the bf16 kernel.
+// Stream-K kernel for e4m3 caches, on the fp8 matrix cores.  The same work
+// list, ranges, segments and merge as the bf16 kernel, with 64-key tiles
+// (four 16-key blocks).  The codes are DMA'd into the ring as they are stored
+// and fed to v_mfma_scale_f32_32x32x64_f8f6f4 as they are: nothing is decoded.
+//
+//   scores  S^T = K . Q^T: A = the K codes of 32 keys x 64 dims, B = Q.  Q is
+//           scaled per row by a power of two 2^-E (its largest |value| into
+//           [128, 256)) and split into two e4m3 terms, hi = e4m3(q) and lo =
+//           e4m3(q - hi), whose products are summed in the same accumulator:
+//           with 4 + 4 significant bits the pair carries Q to about 2^-8,
+//           the precision of bf16 (a single e4m3 term would not).
+//   scale   the K scale of a key's block multiplies its score together with
+//           sm_scale log2(e) 2^E; log2 of the V scale of the block is added to
+//           the exponent, so that the probabilities come out multiplied by the
+//           V scale (the exact decode(code) * scale value of every V element,
+//           applied in fp32) and the running maximum covers that factor too.
+//           l sums the probabilities themselves (each block's sum times the
+//           reciprocal of its V scale).
+//   PV      O^T += V^T . P^T: A = the V codes of 32 dims x 64 keys, B = the
+//           probabilities, again as two e4m3 terms, each row's values scaled
+//           by a power of two that puts the tile's largest into (2^7, 2^8] and
+//           that the MFMA's block scale undoes (without it the small
+//           probabilities of a row would fall into e4m3's subnormals and lose
+//           their precision).
+//
+// Stage layout: K blocks 0..3 as stored ([hd / 16][16 slots][16 dims] each),
+// then V as [dim / 8][block 0..3][dim % 8][16 slots], so that the four blocks'
+// slot rows of one dim lie 128 bytes apart and a lane's V operand is two
+// 16-byte-pair reads (ds_read2_b64) straight into its eight registers.
+//
+// Operand bytes.  For the f8f6f4 MFMA, lane l supplies 32 bytes of A row l %
+// 32 and of B column l % 32, and byte e of lane half h = l / 32 is the same
+// k index in both operands (any one-to-one choice of k(h, e) gives the same
+// product).  Scores use k(h, e) = dim 64 kb + 32 h + e.  The score
+// accumulator of a 32-key half sh puts key 32 sh + 16 (v / 8) + 8 h + v % 8
+// in register v of lane half h (rows fed in the order key_of_row), so PV uses
+// k(h, e) = key 16 (e / 8) + 8 h + e % 8: byte e of the probability operand is
+// then register e % 16 of accumulator e / 16, and byte e of the V operand is
+// slot 8 h + e % 8 of block e / 8 -- eight consecutive bytes of a block's
+// slot row of that dim.
 template <int HD>
-struct SkTile8 {
-  static constexpr int kBlk = HD * 16;       // bytes of one block of e4m3 K or V
-  static constexpr int kStage = 4 * kBlk;    // K blocks 0, 1, then V blocks 0, 1
-  static constexpr int kLoads = kBlk / 1024; // 1 KB wave loads per block
-  static constexpr int kStages = 3;
+struct Sk8 {
+  static constexpr int kKeys = 64;                 // keys per tile
+  static constexpr int kBlk = HD * 16;             // bytes of one 16-key block of K or V codes
+  static constexpr int kStage = 8 * kBlk;          // K blocks 0..3, then V blocks 0..3
+  static constexpr int kStages = SV_STREAM_RING_BYTES / kStage;
+  static constexpr int kLoads = kBlk / 1024;       // 1 KB DMA pieces per block
+  static constexpr int kKb = HD / 64;              // 64-dim k-blocks of the score product
+  static constexpr int kDb = HD / 32;              // 32-dim blocks of O
 };
 
-template <int HD, int WPE, bool NT, bool TREE>
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// D(32x32, fp32) += A(32x64, e4m3) * B(64x32, e4m3), block scales 1.
+__device__ __forceinline__ f32x16 mfma32x32x64_e4m3(const i32x8& a, const i32x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// The same with B scaled by E8M0 exponents sb (low byte): the exponent of lane
+// j scales the first 16 bytes of B column j in both lane halves (lanes j and
+// j + 32), that of lane j + 32 the last 16 bytes, each by 2^(sb - 127).  The
+// callers give lanes j and j + 32 the same exponent: one factor per column.
+__device__ __forceinline__ f32x16 mfma32x32x64_e4m3_sb(const i32x8& a, const i32x8& b, f32x16 c,
+                                                      int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
+// Four fp32 values as four e4m3 codes (round to nearest even; the callers keep
+// every magnitude below 448) in one dword, first value in the lowest byte.
+// `old` is any dword whose value is no longer needed: the conversions write
+// into it in place (both of its halves are overwritten).
+__device__ __forceinline__ int e4m3x4(float a, float b, float c, float d, int old) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// x as hi + lo in e4m3 (hi = e4m3(x), lo = e4m3(x - hi)), four values at a
+// time: the dwords of hi (element 0) and lo (element 1), written over the
+// dead dwords old_hi and old_lo.
+__device__ __forceinline__ u32x2 e4m3_split4(float a, float b, float c, float d, int old_hi,
+                                             int old_lo) {
+  const int hi = e4m3x4(a, b, c, d, old_hi);
+  const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  const int lo = e4m3x4(a - h01[0], b - h01[1], c - h23[0], d - h23[1], old_lo);
+  return u32x2{(uint32_t)hi, (uint32_t)lo};
+}
+
+// Q operands of this lane's row (row_ok: else zeros) as hi and lo e4m3 terms
+// per 64-dim k-block, and the row's score factor c 2^E.
+template <int HD>
+__device__ __forceinline__ void load_q_e4m3(const AttnArgs& a, const RowCtx& r,
+                                            i32x8 (&qhi)[HD / 64], i32x8 (&qlo)[HD / 64],
+                                            float& c_row) {
+  constexpr int KB = HD / 64;
+  const uint16_t* qrow = a.q + ((size_t)(r.b * a.R + r.pos) * a.H_q + r.head) * HD;
+  bf16x8 raw[KB][4];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 z = {};
+      raw[kb][j] = r.row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 64 * kb + 32 * r.hh + 8 * j) : z;
+    }
+  float amax = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[kb][j][e]));
+  amax = halves_max(amax);
+  // amax in [2^(ex-1), 2^ex): q 2^(8-ex) has its largest magnitude in [128, 256)
+  const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 8;
+  c_row = __builtin_amdgcn_ldexpf(a.c, ex - 8);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = __builtin_amdgcn_ldexpf((float)raw[kb][j][e], 8 - ex);
+      const u32x2 a0 = e4m3_split4(v[0], v[1], v[2], v[3], qhi[kb][2 * j], qlo[kb][2 * j]);
+      const u32x2 a1 = e4m3_split4(v[4], v[5], v[6], v[7], qhi[kb][2 * j + 1],
+                                   qlo[kb][2 * j + 1]);
+      qhi[kb][2 * j] = (int)a0[0];
+      qlo[kb][2 * j] = (int)a0[1];
+      qhi[kb][2 * j + 1] = (int)a1[0];
+      qlo[kb][2 * j + 1] = (int)a1[1];
+    }
+}
+
+// Scores of one 32-key half sh of a tile (keys 32 sh + key_of_row(i) in row i).
+template <int HD>
+__device__ __forceinline__ f32x16 sk8_scores(const uint8_t* stage, int k_lds, int sh,
+                                             const i32x8 (&qhi)[HD / 64],
+                                             const i32x8 (&qlo)[HD / 64]) {
+  constexpr int BLK = Sk8<HD>::kBlk;
+  f32x16 x = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < HD / 64; ++kb) {
+    const uint8_t* p = stage + 2 * sh * BLK + k_lds + kb * 1024;
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(p + 256);
+    const i32x8 kop = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                       (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+    x = mfma32x32x64_e4m3(kop, qhi[kb], x);
+    x = mfma32x32x64_e4m3(kop, qlo[kb], x);
+  }
+  return x;
+}
+
+// Key of score register v of lane half hh in half sh of a tile starting at kt.
+__device__ __forceinline__ int sk8_key(int kt, int sh, int v, int hh) {
+  return kt + 32 * sh + 16 * (v >> 3) + 8 * hh + (v & 7);
+}
+
+__device__ __forceinline__ void sk8_mask(f32x16& x, const RowCtx& r, int kt, int sh) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = sk8_key(kt, sh, v, r.hh) > r.vis_last ? -INFINITY : x[v];
+}
+
+// Tree variant: key P + j (a new position, j >= 0) is visible only for the
+// nodes of the row's ancestor mask anc; every term is evaluated for every key
+// (no short-circuit branches around the scores), the shift amount clamped
+// into [0, 63] first.
+__device__ __forceinline__ void sk8_mask_tree(f32x16& x, const RowCtx& r, int kt, int sh,
+                                              uint64_t anc, int R) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int j = sk8_key(kt, sh, v, r.hh) - r.P;
+    const uint32_t s = (uint32_t)min(max(j, 0), 63);
+    const bool in_tree = ((anc >> s) & 1ull) != 0;
+    const bool hidden = (j >= 0) & ((j >= R) | !in_tree);
+    x[v] = hidden ? -INFINITY : x[v];
+  }
+}
+
+// Byte offset of the 16 slot codes of V dim d, block bk in a stage's V part.
+__device__ __forceinline__ int sk8_v_off(int d, int bk) {
+  return ((d >> 3) * 4 + bk) * 128 + (d & 7) * 16;
+}
+
+// Zeroes the V codes of keys >= L in the tile image at stage (keys kt .. kt +
+// 63): poison past the end of the sequence (NaN codes included) must not meet
+// the zero probabilities of those keys in the PV product.
+template <int HD>
+__device__ __forceinline__ void sk8_zero_v_tail(uint8_t* stage, int kt, int L) {
+  constexpr int BLK = Sk8<HD>::kBlk;
+  for (int i = threadIdx.x; i < 4 * HD; i += blockDim.x) {
+    const int bk = i / HD, d = i % HD;
+    const int live = L - (kt + 16 * bk);             // slots of this block before the end
+    if (live < 16) {
+      u32x4* p = reinterpret_cast<u32x4*>(stage + 4 * BLK + sk8_v_off(d, bk));
+      u32x4 v = *p;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int by = 0; by < 4; ++by)
+          if (4 * w + by < live) m |= 0xFFu << (8 * by);
+        v[w] &= m;
+      }
+      *p = v;
+    }
+  }
+}
+
+// Online-softmax update for one 64-key tile (x[sh]: scores of half sh) with the
+// per-block factors cb (K scale * c 2^E), lv (log2 of the V scale) and rv (its
+// reciprocal); the probabilities come out as the PV operand's hi and lo e4m3
+// terms, written over the previous tile's (dead) operands.  A row's 64
+// probabilities are multiplied by a power of two 2^s that puts the tile's
+// largest in (2^7, 2^8] -- well inside e4m3's normal range, so that small ones
+// keep their 4 + 4 bits instead of falling into subnormals -- and sb receives
+// the E8M0 exponent 127 - s that the PV MFMA applies to undo it (the same in
+// both lanes of the row).  Returns whether O must be rescaled by alpha (lazy
+// reference, as in softmax_sub).
+__device__ __forceinline__ bool softmax_tile8(const f32x16 (&x)[2], const float (&cb)[4],
+                                              const float (&lv)[4], const float (&rv)[4],
+                                              float& m_ref, float& l_run, float& alpha,
+                                              i32x8& phi, i32x8& plo, int& sb) {
+  float hm[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x16& xs = x[b >> 1];
+    const int o = 8 * (b & 1);
+    float m = fmaximum(xs[o], xs[o + 1]);
+#pragma unroll
+    for (int v = 2; v < 8; ++v) m = fmaximum(m, xs[o + v]);
+    hm[b] = __builtin_fmaf(m, cb[b], lv[b]);
+  }
+  const float lane_max = fmaximum(fmaximum(hm[0], hm[1]), fmaximum(hm[2], hm[3]));
+  const float tmax = halves_maximum(lane_max);
+  const bool move = tmax > m_ref + kLazyRescale;   // the running maximum starts at kNoMax
+  alpha = move ? fast_exp2(m_ref - tmax) : 1.f;
+  m_ref = move ? tmax : m_ref;
+  // tmax - m_ref <= kLazyRescale, so s >= 0; a row with every key of the tile
+  // masked (tmax = -inf) takes the largest s, its probabilities are all 0
+  const float gap = m_ref - tmax;
+  const int sh = gap < 100.f ? (int)__builtin_floorf(gap) + 8 : 108;
+  sb = 127 - sh;
+  const float shf = (float)sh;
+  float p[32];
+  float s[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x16& xs = x[b >> 1];
+    const int o = 8 * (b & 1);
+    const float ab = (lv[b] - m_ref) + shf;
+    s[b] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const float pv = fast_exp2(__builtin_fmaf(xs[o + v], cb[b], ab));
+      p[8 * b + v] = pv;
+      s[b] += pv;
+    }
+  }
+  l_run = l_run * alpha +
+          __builtin_amdgcn_ldexpf((s[0] * rv[0] + s[1] * rv[1]) + (s[2] * rv[2] + s[3] * rv[3]), -sh);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const u32x2 hl = e4m3_split4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3], phi[w], plo[w]);
+    phi[w] = (int)hl[0];
+    plo[w] = (int)hl[1];
+  }
+  return __ballot(move) != 0;
+}
+
+// O^T += V^T . P^T for one tile (V codes of the stage, keys >= L zeroed).
+template <int HD>
+__device__ __forceinline__ void sk8_pv(const uint8_t* stage, int v_lds, const i32x8& phi,
+                                       const i32x8& plo, int sb, f32x16 (&o)[HD / 32]) {
+  constexpr int BLK = Sk8<HD>::kBlk;
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db) {
+    i32x8 vop;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {   // dims 32 db .. lie 4 x 512 bytes further per block of 32
+      const u32x2 w = *reinterpret_cast<const u32x2*>(stage + 4 * BLK + v_lds + db * 2048 + b * 128);
+      vop[2 * b] = (int)w[0];
+      vop[2 * b + 1] = (int)w[1];
+    }
+    o[db] = mfma32x32x64_e4m3_sb(vop, phi, o[db], sb);
+    o[db] = mfma32x32x64_e4m3_sb(vop, plo, o[db], sb);
+  }
+}
+
+template <int HD, bool NT, bool TREE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kLdsThreads, kLdsThreads),
-                          amdgpu_waves_per_eu(WPE, WPE)))
-void sv_attn_streamk_fp8(AttnArgs a) {
-  constexpr int KS = HD / 16;
-  constexpr int DB = HD / 32;
-  constexpr int BLK = SkTile<HD>::kBlk;      // bf16 image
-  constexpr int STAGE = SkTile<HD>::kStage;
-  constexpr int BLK8 = SkTile8<HD>::kBlk;    // e4m3 ring
-  constexpr int STAGE8 = SkTile8<HD>::kStage;
-  constexpr int LPB = SkTile8<HD>::kLoads;
-  constexpr int NS8 = SkTile8<HD>::kStages;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring8[NS8 * STAGE8];
-  __shared__ __attribute__((aligned(1024))) uint8_t img[3 * STAGE];
-  __shared__ f32x4 s_mant[3];                 // per image: mantissas of K0, K1, V0, V1 scales
-  __shared__ float s_sink[kLdsThreads];       // put_mant's stores by lanes other than 0
-  // the prefix table lives in the images until the first tile is decoded
-  static_assert((kStreamMaxBatch + 1 + kLdsThreads / kWave) * 4 <= 3 * STAGE, "prefix table fits");
-  static_assert(NS8 == 3, "the prologue below fills a three-stage code ring");
-  int* s_pref = reinterpret_cast<int*>(img);
+                          amdgpu_waves_per_eu(2, 2)))
+void sv_attn_streamk_f8(AttnArgs a) {
+  using T8 = Sk8<HD>;
+  constexpr int KEYS = T8::kKeys;
+  constexpr int KB = T8::kKb;
+  constexpr int DB = T8::kDb;
+  constexpr int BLK = T8::kBlk;
+  constexpr int STAGE = T8::kStage;
+  constexpr int NS = T8::kStages;
+  constexpr int LPB = T8::kLoads;
+  static_assert(NS >= 4, "the ring holds the computed tile, the next one and two in flight");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  // per stage: K scale, log2 of the V scale and its reciprocal of blocks 0..3
+  __shared__ f32x4 s_scale[NS][3];
+  __shared__ float s_sink[kLdsThreads];       // scale stores by lanes other than 0
+  static_assert((kStreamMaxBatch + 1 + 4) * 4 <= NS * STAGE, "prefix table fits");
+  int* s_pref = reinterpret_cast<int*>(smem);
   int* s_wsum = s_pref + kStreamMaxBatch + 1;
 
-  build_prefix(a, s_pref, s_wsum);
+  build_prefix<KEYS>(a, s_pref, s_wsum);
   const int W = uniform(s_pref[a.B]);
   const int Wp = max((W + (int)gridDim.x - 1) / (int)gridDim.x, a.min_tiles);
   const int tid = threadIdx.x;
@@ -1421,84 +1659,65 @@ void sv_attn_streamk_fp8(AttnArgs a) {
   const int wave = uniform(tid / kWave);
   const int lane = tid % kWave;
   const int ql = lane & 31, hh = lane >> 5;
-  const size_t blk_stride = (size_t)a.H_kv * BLK8;
+  const uint32_t blk_stride32 = (uint32_t)a.H_kv * BLK;   // below 2^32 (the planner checks)
+  const SV_CONST float* ksc = (const SV_CONST float*)a.k_scale;
+  const SV_CONST float* vsc = (const SV_CONST float*)a.v_scale;
 
-  // Wave w moves (and decodes) block w % 2 of the tile's K (w < 2) or V (w >= 2).
-  const bool moves_v = wave >= 2;
-  const uint8_t* src = moves_v ? a.v : a.k;
-  const SV_CONST float* scales = (const SV_CONST float*)(moves_v ? a.v_scale : a.k_scale);
-  const int k_lds = (ql >> 4) * BLK + (ql & 15) * 16 + hh * 256;
-  const int v_lds = (2 * ql + (hh ^ vhalf_swz(ql))) * 16;
+  // Operand offsets of this lane inside a stage: K row ql of a 32-key half is
+  // key key_of_row(ql) (block ql / 16 of the half, slot key_of_row(ql) % 16),
+  // dims 32 hh .. of each k-block; V dim ql of each 32-dim block, slots 8 hh ..
+  const int k_lds = (ql >> 4) * BLK + ((2 * hh) * 16 + (key_of_row(ql) & 15)) * 16;
+  const int v_lds = sk8_v_off(ql, 0) + 8 * hh;
 
-  // Table entry of this wave's block of the tile at c (a scalar load, as in
-  // the bf16 kernel; entries past the sequence's last block may be read).
-  auto entry = [&](const Cursor& c) -> int {
+  // Table entries of the tile's four blocks, read with scalar loads one tile
+  // ahead (as in the bf16 kernel).  Wave w moves K block w as stored, and 1 KB
+  // pieces of the V part: lane i of piece j holds V dim 8 (2 j + i / 32) + i % 8
+  // of block (i / 8) % 4, so its source block is chosen per lane.
+  auto entry = [&](const Cursor& c) -> i32x4 {
     const SV_CONST int32_t* row = (const SV_CONST int32_t*)c.row;
-    return row[(unsigned)min(2 * c.tile + (wave & 1), a.max_blocks - 1)];
+    const unsigned last = (unsigned)(a.max_blocks - 1);
+    const unsigned j = 4u * (unsigned)c.tile;
+    return i32x4{row[min(j, last)], row[min(j + 1, last)], row[min(j + 2, last)], row[min(j + 3, last)]};
   };
-  // Codes of one tile into ring stage `stage` (linear copy of the block); the
-  // block's scale is returned (a scalar load, first used a tile later).
-  // K codes land in the ring with the slots of each 16-dim group permuted like
-  // the image (bits 2 and 3 of the slot swapped), so that the decode reads and
-  // writes 16-byte vectors in lane order (writes in image order spread eight
-  // consecutive lanes over two 64-byte halves of 128 bytes: a bank conflict).
-  // The permutation stays inside 256 bytes, so one offset serves every 1 KB piece.
-  const uint32_t blk_stride32 = (uint32_t)blk_stride;   // below 2^32 (the planner checks)
-  const int g_off8 = moves_v ? lane * 16 : ((lane >> 4) * 16 + swap23(lane & 15)) * 16;
-  auto issue = [&](const Cursor& c, int raw, int stage) -> float {
-    const uint32_t pb = (uint32_t)min(max(raw, 0), a.num_blocks - 1);
-    const uint8_t* g = src + ((uint64_t)pb * blk_stride32 + (uint32_t)(c.kvh * BLK8));
-    const uint32_t l = lds_addr(ring8) + stage * STAGE8 + wave * BLK8;
-    dma_to_lds16_run<NT, LPB>(g + g_off8, l);
-    return scales[pb * (uint32_t)a.H_kv + (uint32_t)c.kvh];
-  };
-  // Decoding this wave's block of a tile: the codes of ring stage `stage`
-  // (read first, so that the conversion can overlap MFMA work), then their
-  // bf16 values into image `im`.  V past the end of the sequence is zeroed
-  // later, on the image, for the sequence's last tile only.
-  auto dec_read = [&](int stage, u32x4 (&raw)[LPB]) {
-    const uint8_t* s8 = ring8 + stage * STAGE8 + wave * BLK8;
+  constexpr int VPW = BLK / 1024;             // V pieces per wave (4 waves x VPW = 4 BLK / 1 KB)
+  const int vb_lane = (lane >> 3) & 3;        // block of this lane's V piece rows
+  const int vd_lane = (lane & 7) + 8 * (lane >> 5);   // dim within a piece's 16 dims
+  // Loads of one tile into stage `stage`; this wave's block's K and V scales
+  // come back (scalar loads, stored to LDS for all waves an iteration later).
+  auto issue = [&](const Cursor& c, const i32x4& raw, int stage, float& sk, float& sv) {
+    const uint32_t last = (uint32_t)(a.num_blocks - 1);
+    const uint32_t pw = (uint32_t)min(max(raw[wave], 0), (int)last);
+    const uint32_t head = (uint32_t)(c.kvh * BLK);
+    const uint32_t l = lds_addr(smem) + stage * STAGE;
+    dma_to_lds16_run<NT, LPB>(a.k + ((uint64_t)pw * blk_stride32 + head + (uint32_t)lane * 16u),
+                              l + wave * BLK);
+    const int rl = vb_lane == 0 ? raw[0] : vb_lane == 1 ? raw[1] : vb_lane == 2 ? raw[2] : raw[3];
+    const uint32_t pl = (uint32_t)min(max(rl, 0), (int)last);
+    const uint8_t* vsrc = a.v + ((uint64_t)pl * blk_stride32 + head);
 #pragma unroll
-    for (int j = 0; j < LPB; ++j) raw[j] = *reinterpret_cast<const u32x4*>(s8 + (j * kWave + lane) * 16);
-  };
-  // Image offsets of the two bf16 vectors each code vector becomes (K: 16
-  // dims of the key slot image position p % 16 holds; V: 16 key slots of dim
-  // p), fixed per lane.
-  int off_lo[LPB], off_hi[LPB];
-#pragma unroll
-  for (int j = 0; j < LPB; ++j) {
-    const int p = j * kWave + lane;
-    const int k_off = ((2 * (p >> 4)) * 16 + (p & 15)) * 16;
-    off_lo[j] = wave * BLK + (moves_v ? (2 * p + vhalf_swz(p)) * 16 : k_off);
-    off_hi[j] = wave * BLK + (moves_v ? (2 * p + (1 ^ vhalf_swz(p))) * 16 : k_off + 256);
-  }
-  // The scale's power of two goes into the conversion; its mantissa is kept
-  // for the softmax (put_mant, a store by one lane: kept out of the compute
-  // block, whose instruction schedule a branch would split).
-  auto dec_write = [&](const u32x4 (&raw)[LPB], int im, float scale) {
-    uint8_t* dst = img + im * STAGE;             // K blocks 0, 1 then V blocks 0, 1
-    float pow2, mant;
-    split_scale(scale, pow2, mant);
-#pragma unroll
-    for (int j = 0; j < LPB; ++j) {
-      u32x4 lo, hi;
-      e4m3x16_pow2_bf16(raw[j], pow2, lo, hi);
-      *reinterpret_cast<u32x4*>(dst + off_lo[j]) = lo;
-      *reinterpret_cast<u32x4*>(dst + off_hi[j]) = hi;
+    for (int j = 0; j < VPW; ++j) {
+      const int piece = wave * VPW + j;
+      dma_to_lds16<NT>(vsrc + (16 * piece + vd_lane) * 16, l + 4 * BLK + piece * 1024);
     }
+    const uint32_t si = pw * (uint32_t)a.H_kv + (uint32_t)c.kvh;
+    sk = ksc[si];
+    sv = vsc[si];
   };
-  auto put_mant = [&](int im, float scale) {
-    float pow2, mant;
-    split_scale(scale, pow2, mant);
-    // lane 0 stores into the slot, the others into sinks of their own: one
-    // store, no branch
-    float* dst = lane == 0 ? reinterpret_cast<float*>(&s_mant[im]) + wave : &s_sink[tid];
-    *dst = mant;
+  // This wave's block factors of a tile into s_scale[stage][.][wave]: one
+  // store per lane (lane 0 to the slot, the others to sinks), no branch.
+  auto put_scale = [&](int stage, float sk, float sv) {
+    float* d0 = lane == 0 ? reinterpret_cast<float*>(&s_scale[stage][0]) + wave : &s_sink[tid];
+    float* d1 = lane == 0 ? reinterpret_cast<float*>(&s_scale[stage][1]) + wave : &s_sink[tid];
+    float* d2 = lane == 0 ? reinterpret_cast<float*>(&s_scale[stage][2]) + wave : &s_sink[tid];
+    *d0 = sk;
+    *d1 = __builtin_amdgcn_logf(sv);
+    *d2 = __builtin_amdgcn_rcpf(sv);
   };
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
   Cursor cc = ci;                             // tile being computed
-  __syncthreads();                            // the prefix table is dead: images may be written
+  __syncthreads();                            // the prefix table is dead: the ring may fill
+
   auto seg_ctx = [&](const Cursor& c, RowCtx& rr) -> bool {
     const int m0 = c.mt * kStreamRows + wave * kRowsPerWave;
     const int L = clamp_len_s(a, c.b);
@@ -1506,146 +1725,118 @@ void sv_attn_streamk_fp8(AttnArgs a) {
     rr.k_end = L;
     return m0 < a.M;
   };
-  RowCtx r, rn;                                // segment of tile g; the next segment
-  bool active = seg_ctx(cc, r), active_n = false;
+  RowCtx r;
+  bool active = seg_ctx(cc, r);
   int seg_start = g0;
-  bf16x8 qop[KS], qn[KS];
-  if (active) load_q<HD, false>(a, r, qop);
+  i32x8 qhi[KB], qlo[KB];
+  float c_row = a.c;
+  uint64_t anc = 0;
+  if (active) load_q_e4m3<HD>(a, r, qhi, qlo, c_row);
+  if constexpr (TREE) anc = tree_masks(a)[(size_t)r.b * a.R + r.pos];
   wait_vmcnt<0>();                             // Q before the ring's loads, waited once
 
-  // Tile t of the range (t = g - g0) is decoded into image t % 3 two tiles
-  // ahead of its computation; its scores are computed (MFMA) one tile ahead,
-  // under the softmax of the tile before it, as in the bf16 kernel.  sq holds
-  // the scales of the tiles loaded but not yet decoded, oldest first.  The
-  // code ring has three stages too: i0, i1, i2 = t, t + 1, t + 2 modulo 3
-  // index both, rotated once per tile.
   int gi = g0;
-  int ent = entry(ci);
-  float sq[NS8];
-  auto load_next = [&](int stage) -> float {  // past the range: the last tile again
-    const float sc = issue(ci, ent, stage);
-    if (gi + 1 < g1) cursor_next(a, ci);
+  i32x4 ent = entry(ci);
+  float sk_next = 0.f, sv_next = 1.f;          // scales of the tile issued last
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k) {         // past the range: the last tile again
+    float sk, sv;
+    issue(ci, ent, k, sk, sv);
+    if (k < NS - 2) put_scale(k, sk, sv);
+    else { sk_next = sk; sv_next = sv; }
+    if (gi + 1 < g1) cursor_next<KEYS>(a, ci);
     ++gi;
     ent = entry(ci);
-    return sc;
-  };
-  auto decode_now = [&](int stage, int im, float scale) {
-    u32x4 raw[LPB];
-    dec_read(stage, raw);
-    dec_write(raw, im, scale);
-    put_mant(im, scale);
-  };
-#pragma unroll
-  for (int k = 0; k < NS8; ++k) sq[k] = load_next(k);   // tiles 0, 1, 2
-  wait_vmcnt<2 * LPB>();                       // this wave's codes of tile 0
-  decode_now(0, 0, sq[0]);
-  sq[0] = sq[1];
-  sq[1] = sq[2];
-  sq[2] = load_next(0);                        // tile 3
-  wait_vmcnt<2 * LPB>();                       // ... of tile 1
-  decode_now(1, 1, sq[0]);
-  sq[0] = sq[1];
-  sq[1] = sq[2];
-  sq[2] = load_next(1);                        // tile 4
+  }
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  f32x16 xn;                                   // scores of tile g + 1, when have_xn
+  f32x16 xn[2];                                // scores of tile g + 1, when have_xn
   bool have_xn = false;
   float m_ref = kNoMax, l_run = 0.f;
-  int i0 = 0, i1 = 1, i2 = 2;
+  i32x8 phi = {}, plo = {};                    // probability operands (hi, lo) of the last tile
   for (int g = g0; g < g1; ++g) {
-    // this wave's codes of tile g + 2 landed (tiles g + 3, g + 4 may not have:
-    // loads retire in issue order)
-    wait_vmcnt<2 * LPB>();
+    const unsigned t = (unsigned)(g - g0);
+    // This wave's loads of tiles g and g + 1 landed (tile g + 2's may not
+    // have: loads retire in issue order) ...
+    wait_vmcnt<(NS - 3) * 2 * LPB>();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();              // images of tiles g, g + 1 complete; tile g - 1's free
+    __builtin_amdgcn_s_barrier();              // ... and every other wave's; stage g - 1 is free
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-    if (g != g0 && cc.tile == 0) {             // a new segment, prepared one tile ago
+    if (g != g0 && cc.tile == 0) {             // a new segment
       seg_start = g;
-      r = rn;
-      active = active_n;
-      const bf16x8 z = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
+      active = seg_ctx(cc, r);
+      if (active) load_q_e4m3<HD>(a, r, qhi, qlo, c_row);
+      if constexpr (TREE) anc = tree_masks(a)[(size_t)r.b * a.R + r.pos];
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = f32x16{};
       m_ref = kNoMax;
       l_run = 0.f;
       have_xn = false;
     }
-    if (g + 1 < g1 && cc.tile + 1 == cc.T) {   // the next tile starts a segment
-      Cursor cn = cc;
-      cursor_next(a, cn);
-      active_n = seg_ctx(cn, rn);
-      if (active_n) load_q_raw<HD>(a, rn, qn);
-    }
-    // codes of tile g + 2 (decoded in this tile's compute block; past the
-    // range the stage holds the last tile again: decoded, never used)
-    u32x4 raw[LPB];
-    dec_read(i2, raw);
-    const float dscale = sq[0];
-    put_mant(i2, dscale);                      // tile g - 1, the image's last user, is done
+    // the scales of the tile issued last iteration, then this iteration's load
+    put_scale((t + NS - 2) % NS, sk_next, sv_next);
+    issue(ci, ent, (t + NS - 1) % NS, sk_next, sv_next);   // refills the stage of tile g - 1
+    if (gi + 1 < g1) cursor_next<KEYS>(a, ci);
+    ++gi;
+    ent = entry(ci);
 
-    const int kt = cc.tile * kSkKeys;
-    uint8_t* im = img + i0 * STAGE;
-    if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
-      sk_zero_v_tail<HD>(im, kt, r.L);
+    const int kt = cc.tile * KEYS;
+    uint8_t* stage = smem + (t % NS) * STAGE;
+    if (kt + KEYS > r.L) {                     // the sequence's last tile (same for all waves)
+      sk8_zero_v_tail<HD>(stage, kt, r.L);
       __syncthreads();
     }
     if (active) {
-      f32x16 x = have_xn ? xn : sk_scores<HD>(im, k_lds, qop);
-      if (kt + kSkKeys - 1 > r.P) {            // unless every key is visible to every row
-        if constexpr (TREE) sk_mask_tree(x, r, kt, a);
-        else sk_mask(x, r, kt);
+      f32x16 x[2];
+      if (have_xn) {
+        x[0] = xn[0];
+        x[1] = xn[1];
+      } else {
+        x[0] = sk8_scores<HD>(stage, k_lds, 0, qhi, qlo);
+        x[1] = sk8_scores<HD>(stage, k_lds, 1, qhi, qlo);
       }
-      xn = sk_scores<HD>(img + i1 * STAGE, k_lds, qop);
-      const f32x4 mt4 = s_mant[i0];
+      if (kt + KEYS - 1 > r.P) {               // unless every key is visible to every row
+        if constexpr (TREE) {
+          sk8_mask_tree(x[0], r, kt, 0, anc, a.R);
+          sk8_mask_tree(x[1], r, kt, 1, anc, a.R);
+        } else {
+          sk8_mask(x[0], r, kt, 0);
+          sk8_mask(x[1], r, kt, 1);
+        }
+      }
+      const uint8_t* nstage = smem + ((t + 1) % NS) * STAGE;
+      xn[0] = sk8_scores<HD>(nstage, k_lds, 0, qhi, qlo);
+      xn[1] = sk8_scores<HD>(nstage, k_lds, 1, qhi, qlo);
+      const f32x4 skv = s_scale[t % NS][0], lvv = s_scale[t % NS][1], rvv = s_scale[t % NS][2];
+      const float cb[4] = {c_row * skv[0], c_row * skv[1], c_row * skv[2], c_row * skv[3]};
+      const float lv[4] = {lvv[0], lvv[1], lvv[2], lvv[3]};
+      const float rv[4] = {rvv[0], rvv[1], rvv[2], rvv[3]};
       float alpha;
-      bf16x8 p[2];
-      const bool rescale = softmax_sub_fp8(x, a.c * mt4[0], a.c * mt4[1], mt4[2], mt4[3], m_ref,
-                                           l_run, alpha, p[0], p[1]);
-      dec_write(raw, i2, dscale);
-      // probabilities and the decode stay ahead of the rescale branch; the
-      // next tile's score MFMAs interleave with the VALU work
-      asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
-      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);           // DS reads
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);         // VALU
-      }
+      int sb;
+      const bool rescale = softmax_tile8(x, cb, lv, rv, m_ref, l_run, alpha, phi, plo, sb);
+      // Keep the probabilities in this block, ahead of the rescale branch.
+      // (Interleaving the next tile's score MFMAs with this softmax through
+      // schedule groups, as the bf16 kernel does, measured slower here: the
+      // two waves of a SIMD already alternate between their VALU and MFMA
+      // phases.)
+      asm volatile("" : : "v"(phi), "v"(plo), "v"(l_run));
       if (rescale) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
       }
-      // V reads all issued ahead of the PV MFMAs (the score operands are dead)
-      bf16x8 vop[2][DB];
-      sk_read_v<HD>(im, v_lds, vop);
-      sk_pv<HD>(vop, p, o);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);       // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);       // MFMA
-    } else {
-      dec_write(raw, i2, dscale);
+      sk8_pv<HD>(stage, v_lds, phi, plo, sb, o);
     }
     have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
-    // refill the stage just decoded (its codes were consumed above)
-    sq[0] = sq[1];
-    sq[1] = sq[2];
-    sq[2] = load_next(i2);
     if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
       if (active)
         sk_segment_end<HD>(a, r, o, m_ref, l_run,
                            cc.tile == cc.T - 1 && seg_start == g - cc.tile,
                            (int)blockIdx.x * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
-    if (g + 1 < g1) cursor_next(a, cc);
-    const int i_next = i0;
-    i0 = i1;
-    i1 = i2;
-    i2 = i_next;
+    if (g + 1 < g1) cursor_next<KEYS>(a, cc);
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
@@ -1920,7 +2111,8 @@ void plan_attention(AttnPlan& p, int split_request) {
     p.s_max = 1;
     p.sk_rows = p.waves * kRowsPerWave;
     p.sk_wgs = p.waves == 8 ? kStreamCUs : kStreamCUs * kStreamWPE;
-    p.min_tiles = (split_request > 0 ? split_request : kStreamDefaultMinKeys) / kSkKeys;
+    p.min_tiles = (split_request > 0 ? split_request : kStreamDefaultMinKeys) /
+                  (p.fp8 ? Sk8<64>::kKeys : kSkKeys);
     const size_t slots = (size_t)p.sk_wgs * 2 * p.sk_rows;
     p.ws_meta_offset = 0;
     const size_t meta_bytes = ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256;
@@ -1960,9 +2152,9 @@ static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream
   // them once, so they stream past the caches.
   constexpr int S4 = SkTile<HD>::kStages, S8 = SkTile<HD>::kStages8;
   if (p.fp8 && p.m_tiles == 1)
-    sv_attn_streamk_fp8<HD, kStreamWPE, true, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk_f8<HD, true, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.fp8)
-    sv_attn_streamk_fp8<HD, kStreamWPE, false, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
+    sv_attn_streamk_f8<HD, false, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.waves == 8 && p.m_tiles == 1)
     sv_attn_streamk<HD, S8, 2, true, 8, TREE><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
   else if (p.waves == 8)

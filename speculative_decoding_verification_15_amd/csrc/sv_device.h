@@ -65,25 +65,4 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-// Sixteen e4m3 codes (little-endian bytes of raw) times a power of two, as
-// bf16: lo holds codes 0..7, hi codes 8..15.  v_cvt_scalef32_pk_bf16_fp8
-// applies only the exponent of its scale operand, so callers pass an exact
-// power of two; every e4m3 value times a power of two in bf16's range is a
-// bf16 value, so nothing rounds.
-__device__ __forceinline__ void e4m3x16_pow2_bf16(u32x4 raw, float pow2, u32x4& lo, u32x4& hi) {
-#define SV_CVT2(w, upper) \
-  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), pow2, (upper)))
-  lo = u32x4{SV_CVT2(raw[0], false), SV_CVT2(raw[0], true), SV_CVT2(raw[1], false), SV_CVT2(raw[1], true)};
-  hi = u32x4{SV_CVT2(raw[2], false), SV_CVT2(raw[2], true), SV_CVT2(raw[3], false), SV_CVT2(raw[3], true)};
-#undef SV_CVT2
-}
-
-// A positive normal scale s = pow2 * mant with pow2 a power of two and mant in
-// [1, 2), both exact (zero and subnormal scales give pow2 = 0, mant = 1).
-__device__ __forceinline__ void split_scale(float s, float& pow2, float& mant) {
-  const uint32_t b = __float_as_uint(s);
-  pow2 = __uint_as_float(b & 0x7F800000u);
-  mant = __uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
-}
-
 }  // namespace sv
