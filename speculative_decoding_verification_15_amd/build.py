@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libspecverify.so")
-SOURCES = ("sv_api.cpp", "sv_attn.hip", "sv_accept.hip", "sv_sample.hip", "sv_append.hip",
+SOURCES = ("sv_api.cpp", "sv_plan.cpp", "sv_attn.hip", "sv_accept.hip", "sv_sample.hip", "sv_append.hip",
            "sv_draft.hip", "sv_ceil.hip")
 ARCH = "gfx950"
 

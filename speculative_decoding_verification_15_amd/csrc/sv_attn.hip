@@ -406,9 +406,6 @@ constexpr int kLdsThreads = 256;
 #define SV_RING_STAGES 2
 #define SV_RING_WPE 2
 #endif
-#ifndef SV_STREAM_WPE
-#define SV_STREAM_WPE 2
-#endif
 
 template <int HD>
 struct LdsTile {
@@ -882,8 +879,6 @@ void sv_attn_partial_ring(AttnArgs a) {
 // flight.  (A fifth stage, which LDS would allow now that the prefix table
 // lives in the ring, measured no faster.)
 // ---------------------------------------------------------------------------
-constexpr int kStreamRows = 128;          // rows per unit of 4 waves x 32 (8-wave units: 256)
-constexpr int kSkKeys = 32;               // keys per stream-K tile
 
 #ifndef SV_STREAM_RING_BYTES
 #define SV_STREAM_RING_BYTES 65536
@@ -1374,7 +1369,7 @@ void sv_attn_streamk(AttnArgs a) {
 // slot row of that dim.
 template <int HD>
 struct Sk8 {
-  static constexpr int kKeys = 64;                 // keys per tile
+  static constexpr int kKeys = kSk8Keys;           // keys per tile
   static constexpr int kBlk = HD * 16;             // bytes of one 16-key block of K or V codes
   static constexpr int kStage = 8 * kBlk;          // K blocks 0..3, then V blocks 0..3
   static constexpr int kStages = SV_STREAM_RING_BYTES / kStage;
@@ -2078,72 +2073,6 @@ __global__ __launch_bounds__(256) void sv_attn_combine(AttnArgs a, int total_row
   } else {
     orow[0] = f32_to_bf16_bits(acc[0] * inv);
   }
-}
-
-// Stream-K variant: LDS stages per workgroup and workgroups per CU.
-constexpr int kStreamWPE = SV_STREAM_WPE;
-constexpr int kStreamCUs = 256;            // MI355X compute units
-constexpr int kStreamDefaultMinKeys = 512;  // least keys per workgroup range
-
-void plan_attention(AttnPlan& p, int split_request) {
-  p.sk_rows = 0;
-  p.sk_wgs = 0;
-  p.G = p.H_q / p.H_kv;
-  p.M = p.G * p.R;
-  // Batches up to kStreamMaxBatch go through the stream-K ring whatever M is:
-  // waves beyond M still move their share of every tile (the K/V stream, not
-  // the MFMA work, sets the pace when few rows share a KV head).  bf16 units
-  // hold 128 rows (4 waves, two workgroups per CU) or, for 129 .. 256 rows per
-  // KV head, 256 rows (8 waves, one workgroup per CU), so that those rows
-  // stream their K and V once instead of twice.  Beyond 256 rows (MQA-like
-  // heads) the row tiles of a KV head share its K/V through L2 and two 4-wave
-  // workgroups per CU hide latency better (measured); e4m3 units hold 128.
-  p.streamk = p.B <= kStreamMaxBatch;
-  const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
-  if (p.streamk)
-    p.waves = (!p.fp8 && p.M > kStreamRows && p.M <= 2 * kStreamRows) ? 8 : 4;
-  else
-    p.waves = waves_needed > 2 ? 4 : waves_needed;
-  p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);
-  if (p.streamk) {
-    // one split per unit as far as the row context goes; ranges come from min_tiles
-    p.split_tokens = (p.max_kv_len + kAttnTile - 1) / kAttnTile * kAttnTile;
-    p.s_max = 1;
-    p.sk_rows = p.waves * kRowsPerWave;
-    p.sk_wgs = p.waves == 8 ? kStreamCUs : kStreamCUs * kStreamWPE;
-    p.min_tiles = (split_request > 0 ? split_request : kStreamDefaultMinKeys) /
-                  (p.fp8 ? Sk8<64>::kKeys : kSkKeys);
-    const size_t slots = (size_t)p.sk_wgs * 2 * p.sk_rows;
-    p.ws_meta_offset = 0;
-    const size_t meta_bytes = ((size_t)(p.B + 3) * sizeof(int) + 255) / 256 * 256;
-    p.ws_o_bytes = slots * p.hd * sizeof(uint16_t);   // fp16 O / (l f)
-    p.ws_ml_offset = meta_bytes + p.ws_o_bytes;
-    p.ws_f_offset = p.ws_ml_offset + slots * sizeof(f32x2);
-    p.ws_bytes = p.ws_f_offset + slots * sizeof(float);
-    return;
-  }
-  int split = split_request;
-  if (split <= 0) {
-    // Aim at roughly 2048 workgroups for the longest sequences (8 per compute
-    // unit) so ragged lengths still fill the chip, with splits of >= 256 keys.
-    const long long units = (long long)p.B * p.H_kv * p.m_tiles;
-    long long per_unit = units >= 2048 ? 1 : (2048 + units - 1) / units;
-    long long s = (p.max_kv_len + per_unit - 1) / per_unit;
-    s = ((s + kAttnTile - 1) / kAttnTile) * kAttnTile;
-    if (s < 256) s = 256;
-    split = (int)s;
-  }
-  p.split_tokens = split;
-  p.s_max = (p.max_kv_len + split - 1) / split;
-  p.ws_meta_offset = 0;
-  if (p.s_max <= 1) {
-    p.ws_o_bytes = p.ws_ml_offset = p.ws_bytes = 0;
-    return;
-  }
-  const size_t rows = (size_t)p.B * p.H_kv * p.s_max * p.M;
-  p.ws_o_bytes = rows * p.hd * sizeof(float);
-  p.ws_ml_offset = (p.ws_o_bytes + 255) / 256 * 256;
-  p.ws_bytes = p.ws_ml_offset + rows * sizeof(f32x2);
 }
 
 template <int HD, bool TREE>

@@ -1,5 +1,5 @@
-// Host-side plan and launcher of spec_verify_attn (sv_attn.hip), shared with
-// the C ABI layer.  Arguments reaching the launcher have been validated.
+// Host-side plan (sv_plan.cpp) and launcher (sv_attn.hip) of spec_verify_attn,
+// shared with the C ABI layer.  Arguments reaching them have been validated.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,6 +14,19 @@ constexpr int kAttnTile = 64;
 constexpr int kStreamMaxBatch = 2048;
 // Query rows per wave (one 32-wide MFMA operand).
 constexpr int kRowsPerWave = 32;
+// Stream-K: rows per unit of 4 waves x 32 (8-wave units: 256), keys per tile
+// of the bf16 kernel and of the e4m3 kernel.
+constexpr int kStreamRows = 128;
+constexpr int kSkKeys = 32;
+constexpr int kSk8Keys = 64;
+// Stream-K grid: workgroups per CU (4-wave units), MI355X compute units, and
+// the least keys per workgroup range.
+#ifndef SV_STREAM_WPE
+#define SV_STREAM_WPE 2
+#endif
+constexpr int kStreamWPE = SV_STREAM_WPE;
+constexpr int kStreamCUs = 256;
+constexpr int kStreamDefaultMinKeys = 512;
 
 struct AttnPlan {
   int B, R, H_q, H_kv, G, M, hd;
