@@ -177,7 +177,7 @@ sv_status spec_verify_attn(const sv_attn_params* p, const void* q, const void* k
  *              topological order, parents before children); bits at or above R
  *              are ignored.
  * Errors: as spec_verify_attn; SV_ERR_INVALID for a NULL or misaligned
- * tree_mask; SV_ERR_UNSUPPORTED for batch > 2048.
+ * tree_mask.
  */
 sv_status spec_verify_attn_tree(const sv_attn_params* p, const void* q, const void* k_cache,
                                 const void* v_cache, const float* k_scale, const float* v_scale,

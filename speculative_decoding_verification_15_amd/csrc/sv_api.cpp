@@ -133,9 +133,6 @@ static sv_status run_attn(const sv_attn_params* p, const void* q, const void* k_
   }
   if (tree_mask && !aligned(tree_mask, 8))
     return fail(SV_ERR_INVALID, "tree_mask must be 8-byte aligned");
-  if (tree_mask && !plan.streamk)
-    return fail(SV_ERR_UNSUPPORTED, "tree verification needs batch <= %d (got %d)",
-                sv::kStreamMaxBatch, p->batch);
   if (plan.ws_bytes > 0) {
     if (!workspace) return fail(SV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan.ws_bytes);
     if (workspace_bytes < plan.ws_bytes)

@@ -61,24 +61,18 @@ struct AttnArgs {
   int B, R, H_q, H_kv, G, M;
   int max_blocks, num_blocks, max_kv_len;
   int split_tokens;
-  union {
-    int s_max;         // split path: splits per sequence
-    uint32_t tree_lo;  // stream-K tree variants: low word of the ancestor-mask pointer
-  };
+  int s_max;      // split path: splits per sequence
   int m_tiles;
   int min_tiles;  // stream-K: least tiles per workgroup
   float c;        // sm_scale * log2(e)
   int* sk_meta;   // stream-K: [W, Wp, pref[0..B]] written by workgroup 0 for the merge
   int sk_rows;    // stream-K: rows per unit (128 or 256)
-  uint32_t tree_hi;  // stream-K tree variants: high word of the ancestor-mask pointer
-                     // (the struct's trailing padding, so the layout is unchanged)
+  const uint64_t* tree;  // NULL: causal chain; else [B][R] ancestor masks
 };
 
-// Tree variants: [B][R] ancestor masks, bit j of mask[b][i] = node j is node i
-// or one of its ancestors.
-__device__ __forceinline__ const uint64_t* tree_masks(const AttnArgs& a) {
-  return reinterpret_cast<const uint64_t*>(((uint64_t)a.tree_hi << 32) | a.tree_lo);
-}
+// Tree verification: [B][R] ancestor masks, bit j of mask[b][i] = node j is
+// node i or one of its ancestors.
+__device__ __forceinline__ const uint64_t* tree_masks(const AttnArgs& a) { return a.tree; }
 
 // Row i of the 32-key score block holds key pi(i) of that block.
 __device__ __forceinline__ int key_of_row(int i) {
@@ -90,12 +84,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Everything one lane needs to know about its query row and key range.
+// Everything one lane needs to know about its query row and key range.  anc:
+// the new positions the row may see (bit j: key P + j), the positions up to its
+// own for a causal chain, its ancestor mask for a draft tree (split-path
+// kernels; the stream-K kernels mask trees themselves).
 struct RowCtx {
   int b, kvh, split, L, n_splits, k_begin, k_end;
-  int m, pos, head, P, vis_last;
+  int m, pos, head, P, vis_last, R;
   int ql, hh;
   bool row_ok;
+  uint64_t anc;
 };
 
 __device__ __forceinline__ RowCtx make_row_ctx(const AttnArgs& a, int split, int kvh, int b,
@@ -116,7 +114,24 @@ __device__ __forceinline__ RowCtx make_row_ctx(const AttnArgs& a, int split, int
   r.head = kvh * a.G + (r.row_ok ? r.m % a.G : 0);
   r.P = L - a.R;
   r.vis_last = r.P + r.pos;
+  r.R = a.R;
+  r.anc = (2ull << r.pos) - 1ull;   // positions 0 .. pos (all 64 bits for pos = 63)
   return r;
+}
+
+// Split-path kernels: the row's ancestor mask replaces the chain mask for a tree.
+__device__ __forceinline__ void load_row_anc(const AttnArgs& a, RowCtx& r) {
+  if (a.tree) r.anc = a.tree[(size_t)r.b * a.R + r.pos];
+}
+
+// Whether key `key` (at or past the first new position P) is hidden from the
+// row: past the end, or a new position outside the row's mask.  Every term is
+// evaluated for every key, the shift amount clamped into [0, 63] first.
+__device__ __forceinline__ bool row_hides(const RowCtx& r, int key) {
+  const int j = key - r.P;
+  const uint32_t s = (uint32_t)min(max(j, 0), 63);
+  const bool in = ((r.anc >> s) & 1ull) != 0;
+  return (j >= 0) & ((j >= r.R) | !in);
 }
 
 __device__ __forceinline__ int clamp_len(const AttnArgs& a, int b) {
@@ -221,7 +236,7 @@ __device__ __forceinline__ bool softmax_core(f32x16 (&x)[2], const float (&cs)[2
       for (int v = 8 * half; v < 8 * half + 8; ++v) {
         if constexpr (MASKED) {
           const int key = kt + 32 * sb + key_of_row(8 * (v >> 2) + 4 * r.hh + (v & 3));
-          if (!live[sb] || key > r.vis_last) x[sb][v] = -INFINITY;
+          if (!live[sb] || row_hides(r, key)) x[sb][v] = -INFINITY;
         }
         hm = fmaxf(hm, x[sb][v]);
       }
@@ -503,7 +518,8 @@ void sv_attn_partial_lds(AttnArgs a) {
   const int lane = tid % kWave;
   const int m0 = (mt * 4 + wave) * kRowsPerWave;
   const bool active = m0 < a.M;                       // inactive waves still load
-  const RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+  RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+  load_row_anc(a, r);
 
   bf16x8 qop[KS];
   if (active) load_q<HD, false>(a, r, qop);
@@ -792,7 +808,8 @@ void sv_attn_partial_ring(AttnArgs a) {
   const int lane = tid % kWave;
   const int m0 = (mt * 4 + wave) * kRowsPerWave;
   const bool active = m0 < a.M;                       // inactive waves still load
-  const RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+  RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+  load_row_anc(a, r);
 
   bf16x8 qop[KS];
   if (active) load_q<HD, false>(a, r, qop);
@@ -1942,7 +1959,8 @@ __global__ __launch_bounds__(kWave * NW) void sv_attn_partial_direct(AttnArgs a)
   const int lane = threadIdx.x % kWave;
   const int m0 = (mt * NW + wave) * kRowsPerWave;
   if (m0 >= a.M) return;
-  const RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+  RowCtx r = make_row_ctx(a, split, kvh, b, L, m0, lane);
+  load_row_anc(a, r);
 
   bf16x8 qop[KS];
   load_q<HD, FP8>(a, r, qop);
@@ -2167,14 +2185,9 @@ hipError_t launch_attention(const AttnPlan& p, const AttnPtrs& ptr, hipStream_t 
   a.s_max = p.s_max;
   a.m_tiles = p.m_tiles;
   a.c = p.sm_scale * kLog2e;
-  a.tree_hi = 0;
-  if (ptr.tree_mask) {
-    if (!p.streamk) return hipErrorInvalidValue;   // the host rejects trees off the stream-K path
-    const uint64_t tm = reinterpret_cast<uint64_t>(ptr.tree_mask);
-    a.tree_lo = (uint32_t)tm;
-    a.tree_hi = (uint32_t)(tm >> 32);
+  a.tree = ptr.tree_mask;
+  if (ptr.tree_mask && p.streamk)
     return p.hd == 128 ? launch_streamk<128, true>(p, a, stream) : launch_streamk<64, true>(p, a, stream);
-  }
   if (p.streamk)
     return p.hd == 128 ? launch_streamk<128, false>(p, a, stream) : launch_streamk<64, false>(p, a, stream);
   if (p.hd == 128)

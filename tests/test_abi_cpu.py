@@ -413,13 +413,15 @@ def test_attn_tree_errors():
     lib = sv.library()
     p = good_params()
 
-    def call(tm, **kw):
+    def call(tm, ws_bytes=1 << 40, **kw):
         pp = good_params(**kw)
         return lib.spec_verify_attn_tree(ctypes.byref(pp), FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
-                                         tm, FAKE * 2, FAKE * 4, 1 << 40, None)
+                                         tm, FAKE * 2, FAKE * 4, ws_bytes, None)
     assert call(None) == sv.SV_ERR_INVALID
     assert call(FAKE + 4) == sv.SV_ERR_INVALID
-    assert call(FAKE, batch=3000) == sv.SV_ERR_UNSUPPORTED        # split-K path: no trees
+    # past the stream-K batch limit a tree takes the split path: the call gets
+    # through the argument checks and stops at the (too small) workspace
+    assert call(FAKE, batch=3000, max_kv_len=1000, split_tokens=256, ws_bytes=16) == sv.SV_ERR_WORKSPACE
     assert call(FAKE, draft_len=64) == sv.SV_ERR_INVALID
     assert p.batch == 4
 

@@ -4,11 +4,14 @@ Attention: every output element against the fp64 oracle with tree visibility,
 max-abs <= 1e-2 and mean-abs <= 1e-3 (as chain attention), on reduced shapes
 (bf16 and e4m3, hd 64 and 128, 16 to 64 nodes, 128- and 256-row units and
 several row tiles per KV head) with random and star trees; at the 70B-like
-shape on sampled sequences.  A chain tree gives spec_verify_attn's output bit
+shape on sampled sequences; more than 2048 sequences (the split-K path) on
+sampled sequences, including contexts shorter than one sub-block.  A chain tree gives spec_verify_attn's output bit
 for bit (same arithmetic, the mask selects the same keys).
 Acceptance: target tokens, AL, out_tokens, accept_path and the committed
 lengths bit-exact against the oracle.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -19,8 +22,8 @@ from oracle.attention import oracle_attn
 from oracle.tree import oracle_accept_tree
 from tests.gpu_util import (MAX_ABS_TOL, MEAN_ABS_TOL, BF16_NAN, DeviceAttn, attn_errors,
                             attn_params, dev, note)
-from workloads import (EDGE, LLAMA31_70B, MINI, make_accept_plan, make_attn_inputs,
-                       make_tree_plan, tree_tokens_from_target)
+from workloads import (EDGE, LLAMA31_70B, MINI, Workload, make_accept_plan, make_attn_inputs,
+                       make_tree_plan, split_path_lengths, tree_tokens_from_target)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +108,45 @@ def test_tree_attention_70b_like_sampled():
     L = inp.kv_lens
     seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 5, 17})
     _check(gpu, _oracle(inp, plan.parents, seqs=seqs), "70b-like/random tree")
+
+
+@functools.lru_cache(maxsize=1)     # consecutive cases differ only in the split size
+def _tree_batch2100_inputs(G, D, kv):
+    w = Workload(f"tree_batch2100_{kv}_g{G}_d{D}", 3003, B=2100, H_q=2 * G, H_kv=2, hd=128, D=D,
+                 T_range=(1, 2000), kv_dtype=kv)
+    T = split_path_lengths(w.B, 3003)
+    T[1::97] = np.random.default_rng(3004).integers(1, 32, len(T[1::97]))
+    return make_attn_inputs(w, T_override=T), make_tree_plan(w, shape="random", width=3)
+
+
+# More than 2048 sequences: tree masks on the split-K path (direct kernel for
+# M = 16, the LDS ring or the register-staged kernel for M = 128), 256-token
+# splits and the automatic choice.  Mostly short contexts with every 64th one
+# long (1000 to 2000 tokens); every 97th is shorter than one 32-key sub-block
+# (1 to 31 tokens), so whole tiles, even whole splits, hold only new positions
+# and some rows see none of a split's keys.  Rows of those very short
+# sequences average a handful of values (|O| up to about 3), whose bf16
+# rounding alone is up to 2^-9 |O|: they are held to max-abs 1e-2 + 2^-8 |O|.
+@pytest.mark.parametrize("split", [256, 0], ids=["split256", "auto"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("G,D", [(4, 3), (8, 15)], ids=["m16", "m128"])
+def test_tree_attention_split_path(G, D, kv, split):
+    inp, plan = _tree_batch2100_inputs(G, D, kv)
+    w, T = inp.w, inp.kv_lens - inp.w.R
+    out, _ = run_tree_attention(inp, plan.masks, split)
+    gpu = DeviceAttn.to_f64(out)
+    assert np.isfinite(gpu).all(), "a row is not finite"
+    rng = np.random.default_rng(12)
+    short = [1, 98, 195]
+    seqs = sorted({int(np.argmin(T)), int(np.argmax(T)), 0, 64, w.B - 1}
+                  | set(rng.integers(0, w.B, 4).tolist()))
+    _check(gpu, _oracle(inp, plan.parents, seqs=[b for b in seqs if T[b] >= 32]),
+           f"{w.name}/split={split}")
+    ref = _oracle(inp, plan.parents, seqs=short)
+    sel = np.isfinite(ref)
+    err = np.abs(gpu[sel] - ref[sel])
+    note(f"  short contexts {T[short].tolist()}: max_abs={err.max():.3e}")
+    assert (err <= MAX_ABS_TOL + 2.0 ** -8 * np.abs(ref[sel])).all()
 
 
 def run_accept_tree(logits, tokens, parents, kv_in, inplace=False):

@@ -6,4 +6,4 @@ from .generate import (AttnInputs, AcceptPlan, make_attn_inputs, make_accept_pla
                        drafts_from_target, f32_to_bf16_bits, f32_to_e4m3_bits, seed_streams,
                        SampledAcceptInputs, make_sampled_accept_inputs, AppendInputs,
                        make_append_inputs, make_draft_logits, TreePlan,
-                       make_tree_plan, tree_tokens_from_target)
+                       make_tree_plan, tree_tokens_from_target, split_path_lengths)

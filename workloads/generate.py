@@ -320,3 +320,13 @@ def tree_tokens_from_target(plan: TreePlan, target: np.ndarray) -> np.ndarray:
         r = plan.other[:, j]
         tok[:, j] = np.where(plan.match[:, j], pt, r + (r >= pt))
     return tok
+
+
+def split_path_lengths(B, seed, long_every=64):
+    """Contexts for the many-sequence split path: mostly short (32 to 200
+    tokens), every ``long_every``-th sequence long (1000 to 2000 tokens), so
+    that 256-token splits cut the long ones into up to eight pieces."""
+    rng = np.random.default_rng(seed)
+    T = rng.integers(32, 201, B)
+    T[::long_every] = rng.integers(1000, 2001, len(T[::long_every]))
+    return T
