@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--split-tokens S] [--no-cpu-baseline]
+    python bench.py --tile-sweep       (spec_verify_attn alone on the 14
+                                        tile-boundary shapes)
 
 One step = one full pass of the hot path over one batch: spec_verify_attn
 (paged GQA attention of the 1 + D verified positions, split-K merge) followed
@@ -328,6 +330,47 @@ def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
             "seconds": round(t_total, 2)}
 
 
+def tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs):
+    """spec_verify_attn alone on the tile-boundary shapes (B=8, T=16384, bf16;
+    H_kv = 8 or 1, D in SWEEP_D): 100 untimed calls, then the best of three runs
+    of 10 calls timed with HIP events on the launch stream."""
+    import torch
+    from workloads import SWEEP_D, tile_sweep
+    stream = torch.cuda.current_stream()
+    for mqa in (False, True):
+        for D in SWEEP_D:
+            w = tile_sweep(D, mqa)
+            inp = make_attn_inputs(w)
+            d = DeviceAttn(inp)
+            p = attn_params(inp)
+            plan_ws = sv.spec_verify_attn_workspace_size(p)
+            ws = torch.empty(max(plan_ws, 256), dtype=torch.uint8, device="cuda")
+            out = torch.empty(d.q.shape, dtype=torch.int16, device="cuda")
+
+            def call():
+                sv.spec_verify_attn(p, d.q, d.k, d.v, d.ks, d.vs, d.bt, d.kl, out, ws, plan_ws,
+                                    stream=stream.cuda_stream)
+            for _ in range(LEG_WARMUP):
+                call()
+            best = float("inf")
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(10):
+                    call()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                best = min(best, e0.elapsed_time(e1) * 1e3 / 10)
+            kv = attn_algorithmic_kv_bytes(inp)
+            fl = attn_algorithmic_flops(inp)
+            print(json.dumps({"tile_sweep": w.name, "M": w.M, "us": round(best, 1),
+                              "kv_GBps": round(kv / (best * 1e-6) / 1e9, 1),
+                              "TFLOPs": round(fl / (best * 1e-6) / 1e12, 1),
+                              "frac_bf16_peak": round(fl / (best * 1e-6) / 1e12 /
+                                                      BF16_MFMA_PEAK_TFLOPS, 4)}), flush=True)
+            del d, ws, out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +382,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy (reference for HBM counters)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="only time spec_verify_attn on the 14 tile-boundary shapes (one JSON "
+                         "line each)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -361,6 +407,10 @@ def main():
     import speculative_decoding_verification_15_amd as sv
     from speculative_decoding_verification_15_amd.device import DeviceAttn, attn_params, dev
     from workloads import all_workloads, drafts_from_target, make_accept_plan, make_attn_inputs
+
+    if args.tile_sweep:
+        tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs)
+        return
 
     w = all_workloads()[args.workload]
     assert w.V > 0, "the benchmark step needs an acceptance vocabulary"

@@ -111,9 +111,9 @@ def test_tree_attention_70b_like_sampled():
 
 
 @functools.lru_cache(maxsize=1)     # consecutive cases differ only in the split size
-def _tree_batch2100_inputs(G, D, kv):
-    w = Workload(f"tree_batch2100_{kv}_g{G}_d{D}", 3003, B=2100, H_q=2 * G, H_kv=2, hd=128, D=D,
-                 T_range=(1, 2000), kv_dtype=kv)
+def _tree_batch2100_inputs(hd, G, D, kv):
+    w = Workload(f"tree_batch2100_hd{hd}_{kv}_g{G}_d{D}", 3003, B=2100, H_q=2 * G, H_kv=2, hd=hd,
+                 D=D, T_range=(1, 2000), kv_dtype=kv)
     T = split_path_lengths(w.B, 3003)
     T[1::97] = np.random.default_rng(3004).integers(1, 32, len(T[1::97]))
     return make_attn_inputs(w, T_override=T), make_tree_plan(w, shape="random", width=3)
@@ -130,8 +130,9 @@ def _tree_batch2100_inputs(G, D, kv):
 @pytest.mark.parametrize("split", [256, 0], ids=["split256", "auto"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("G,D", [(4, 3), (8, 15)], ids=["m16", "m128"])
-def test_tree_attention_split_path(G, D, kv, split):
-    inp, plan = _tree_batch2100_inputs(G, D, kv)
+@pytest.mark.parametrize("hd", [64, 128])
+def test_tree_attention_split_path(hd, G, D, kv, split):
+    inp, plan = _tree_batch2100_inputs(hd, G, D, kv)
     w, T = inp.w, inp.kv_lens - inp.w.R
     out, _ = run_tree_attention(inp, plan.masks, split)
     gpu = DeviceAttn.to_f64(out)
