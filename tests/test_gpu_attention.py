@@ -190,6 +190,19 @@ def test_split_path_above_2048_sequences(hd, G, D, kv, split):
     _sampled_check(inp, f"{w.name}/split={split}", split=split, extra=(64, 128, 1024))
 
 
+# The stream-K path at its largest batch (2048 sequences: the per-sequence tile
+# prefix fills its LDS table): 4-wave 128-row units (bf16 and e4m3) and 8-wave
+# 256-row units (bf16, 192 rows per KV head).
+@pytest.mark.parametrize("kv,G,D", [(KV_BF16, 8, 15), (KV_FP8, 8, 15), (KV_BF16, 8, 23)],
+                         ids=["bf16_m128", "fp8_m128", "bf16_m192"])
+def test_streamk_at_max_batch(kv, G, D):
+    w = Workload(f"batch2048_{kv}_g{G}_d{D}", 3005, B=2048, H_q=G, H_kv=1, hd=128, D=D,
+                 T_range=(32, 2000), kv_dtype=kv)
+    inp = make_attn_inputs(w, T_override=split_path_lengths(w.B, 3005))
+    assert sv.spec_verify_attn_workspace_size(attn_params(inp)) > 0
+    _sampled_check(inp, w.name, extra=(64, 128, 2047))
+
+
 # Many short sequences on the stream-K path: most 32-key tiles start or end a
 # segment, whole units finish inside ranges, and ranges cut units of two tiles
 # (contexts from 32 tokens, as above).

@@ -150,6 +150,20 @@ def test_tree_attention_split_path(hd, G, D, kv, split):
     assert (err <= MAX_ABS_TOL + 2.0 ** -8 * np.abs(ref[sel])).all()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"], ids=["bf16", "fp8"])
+def test_tree_attention_streamk_max_batch(kv):
+    """2048 sequences, the largest batch of the stream-K tree kernels."""
+    w = Workload(f"tree_batch2048_{kv}", 3006, B=2048, H_q=8, H_kv=1, hd=128, D=15,
+                 T_range=(32, 2000), kv_dtype=kv)
+    inp = make_attn_inputs(w, T_override=split_path_lengths(w.B, 3006))
+    plan = make_tree_plan(w, shape="random", width=3)
+    gpu = DeviceAttn.to_f64(run_tree_attention(inp, plan.masks)[0])
+    assert np.isfinite(gpu).all(), "a row is not finite"
+    T = inp.kv_lens - w.R
+    seqs = sorted({int(np.argmin(T)), int(np.argmax(T)), 0, 64, 1000, w.B - 1})
+    _check(gpu, _oracle(inp, plan.parents, seqs=seqs), w.name)
+
+
 def run_accept_tree(logits, tokens, parents, kv_in, inplace=False):
     B, R, V = logits.shape
     D = R - 1
