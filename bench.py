@@ -364,7 +364,9 @@ def tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs):
                 best = min(best, e0.elapsed_time(e1) * 1e3 / 10)
             kv = attn_algorithmic_kv_bytes(inp)
             fl = attn_algorithmic_flops(inp)
-            print(json.dumps({"tile_sweep": w.name, "M": w.M, "us": round(best, 1),
+            m_pad = -(-w.M // 128) * 128              # rows rounded to 128-row tiles
+            print(json.dumps({"tile_sweep": w.name, "M": w.M, "M_pad": m_pad, "us": round(best, 1),
+                              "TFLOPs_padded": round(fl * m_pad / w.M / (best * 1e-6) / 1e12, 1),
                               "kv_GBps": round(kv / (best * 1e-6) / 1e9, 1),
                               "TFLOPs": round(fl / (best * 1e-6) / 1e12, 1),
                               "frac_bf16_peak": round(fl / (best * 1e-6) / 1e12 /
@@ -546,6 +548,7 @@ def main():
                              "all": [round(float(x), 1) for x in attn_steps]},
         "step_ms_median": round(float(np.median(t_attn + t_acc)), 4),
         "kv_hbm_GBps": round(kv_gbps, 1),
+        "scored_rows_per_s": round(B * R / (attn_us * 1e-6), 1),
         "kv_hbm_frac_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "mfma": ({"type": "bf16", "achieved_tflops": round(tflops, 1),
                   "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
