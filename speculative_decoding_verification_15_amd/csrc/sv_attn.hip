@@ -2097,7 +2097,11 @@ template <int HD, bool TREE>
 static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream_t stream) {
   // Row tiles of one KV head share its K/V through L2; a lone row tile reads
   // them once, so they stream past the caches.
+  // Units of at most 64 rows (two of the four waves compute, or fewer) stream
+  // faster with one tile fewer in flight: 3 stages for hd 128.
   constexpr int S4 = SkTile<HD>::kStages, S8 = SkTile<HD>::kStages8;
+  constexpr int S3 = HD == 128 ? 3 : S4;
+  const bool few_rows = p.M <= 2 * kRowsPerWave;
   if (p.fp8 && p.m_tiles == 1)
     sv_attn_streamk_f8<HD, true, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.fp8)
@@ -2106,6 +2110,8 @@ static hipError_t launch_streamk(const AttnPlan& p, const AttnArgs& a, hipStream
     sv_attn_streamk<HD, S8, 2, true, 8, TREE><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
   else if (p.waves == 8)
     sv_attn_streamk<HD, S8, 2, false, 8, TREE><<<p.sk_wgs, 8 * kWave, 0, stream>>>(a);
+  else if (p.m_tiles == 1 && few_rows)
+    sv_attn_streamk<HD, S3, kStreamWPE, true, 4, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else if (p.m_tiles == 1)
     sv_attn_streamk<HD, S4, kStreamWPE, true, 4, TREE><<<p.sk_wgs, kLdsThreads, 0, stream>>>(a);
   else
