@@ -282,7 +282,7 @@ def measure_ceilings(stream, sv):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")   # values are never used
     sink = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
     read = {}
-    for wgs in (1024, 2048, 4096):
+    for wgs in (nbytes // 16384, 16384, 4096):    # one, four or sixteen 16 KB chunks each
         us = best_us(lambda: sv.sv_ceiling_read(src, nbytes, wgs, sink, stream=sh))
         read[wgs] = nbytes / (us * 1e-6) / 1e9
     wgs = max(read, key=read.get)
@@ -295,8 +295,8 @@ def measure_ceilings(stream, sv):
     e_wgs, e_it = 2048, 512
     us = best_us(lambda: sv.sv_ceiling_exp2(e_wgs, e_it, sink, stream=sh))
     out["exp2_per_s"] = float(f"{e_wgs * 256 * e_it * 8 / (us * 1e-6):.4g}")
-    out["method"] = ("sv_ceiling_read (16-byte non-temporal loads, best of 1024/2048/4096 "
-                     "workgroups), sv_ceiling_mfma_bf16 (4 independent 32x32x16 bf16 MFMA chains "
+    out["method"] = ("sv_ceiling_read (16-byte non-temporal loads, 16 KB per workgroup at a "
+                     "time, best of 65536/16384/4096 workgroups), sv_ceiling_mfma_bf16 (4 independent 32x32x16 bf16 MFMA chains "
                      "per wave), sv_ceiling_exp2 (8 independent v_exp_f32 chains per thread); "
                      "best of 5 launches each, after the timed steps")
     return out

@@ -29,8 +29,10 @@ extern "C" {
 
 /* Streaming read: every byte of src[0 .. bytes) is read once with 16-byte
  * non-temporal vector loads by a grid of `workgroups` x 256 threads
- * (workgroups in [1, 65536]); bytes > 0 and a multiple of 16, src 16-byte
- * aligned.  One float per workgroup (a reduction of the values read, so the
+ * (workgroups in [1, 65536]), each workgroup reading whole 16 KB chunks (the
+ * chunks w, w + workgroups, ... for workgroup w; what follows the last whole
+ * chunk is read one vector per thread); bytes > 0 and a multiple of 16, src
+ * 16-byte aligned.  One float per workgroup (a reduction of the values read, so the
  * loads cannot be dropped) goes to sink[0 .. workgroups).  Rate = bytes /
  * kernel time. */
 sv_status sv_ceiling_read(const void* src, size_t bytes, int32_t workgroups, float* sink,

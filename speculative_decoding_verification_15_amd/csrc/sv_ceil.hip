@@ -8,22 +8,29 @@ namespace sv {
 
 constexpr int kCeilThreads = 256;
 
-// Every 16-byte vector of src read once: consecutive threads take consecutive
-// vectors, four vectors in flight per thread.  The words are folded with XOR
-// (no float work) and one value per workgroup is stored so the loads stay.
+// Every 16-byte vector of src read once, 16 KB at a time per workgroup:
+// workgroup w takes the chunks w, w + gridDim.x, ..., each thread four
+// vectors 4 KB apart inside a chunk (a wave reads 1 KB runs), all four in
+// flight; vectors past the last whole chunk go round the grid one per thread.
+// The words are folded with XOR (no float work) and one value per workgroup
+// is stored so the loads stay.  (A grid-stride pattern whose four loads per
+// thread lie a grid apart read ~12% slower on these GPUs.)
+constexpr size_t kCeilChunk = 1024;         // 16-byte vectors per chunk
+
 __global__ __launch_bounds__(kCeilThreads) void sv_ceil_read(const u32x4* __restrict__ src,
                                                              size_t n, float* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * kCeilThreads;
-  size_t i = (size_t)blockIdx.x * kCeilThreads + threadIdx.x;
+  const size_t chunks = n / kCeilChunk;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n; i += 4 * stride) {
+  for (size_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+    const u32x4* p = src + c * kCeilChunk + threadIdx.x;
     u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + u * kCeilThreads);
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n; i += stride) {
+  for (size_t i = chunks * kCeilChunk + (size_t)blockIdx.x * kCeilThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kCeilThreads) {
     const u32x4 v = __builtin_nontemporal_load(src + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
