@@ -44,6 +44,56 @@ KERNEL_SOURCES = ("speculative_decoding_verification_15_amd/csrc/sv_attn.hip",
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sv_attn.md")
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence.
+
+    Its record skips the system-scope cache write-back a default event makes:
+    the default event torch creates adds ~3 us of stream time per record between
+    two kernels here, ~1.5 us with this flag.  The runtime is the libamdhip64
+    torch has already loaded (the library's own soname), so the stream handles
+    are the ones torch and the library use.  Same calls as torch.cuda.Event.
+    """
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                    ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._h = ctypes.c_void_p()
+        self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(self._h),
+                                                      self.DISABLE_SYSTEM_FENCE), "create")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"hipEvent{what} failed with hipError {rc}")
+
+    def record(self, stream):
+        import ctypes
+        self._check(self._hip.hipEventRecord(self._h, ctypes.c_void_p(stream.cuda_stream)),
+                    "Record")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        self._check(self._hip.hipEventElapsedTime(ctypes.byref(ms), self._h, end._h),
+                    "ElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._h:
+            self._hip.hipEventDestroy(self._h)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -127,7 +177,7 @@ def time_append(w, da, stream, sv, calls=20):
     sh = stream.cuda_stream
     for _ in range(LEG_WARMUP):        # the GPU idled during input generation: clocks ramp up
         sv.spec_kv_append(prm, kn, vn, da.k, da.v, da.ks, da.vs, da.bt, kin, kout, stream=sh)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(calls):
         sv.spec_kv_append(prm, kn, vn, da.k, da.v, da.ks, da.vs, da.bt, kin, kout, stream=sh)
@@ -164,7 +214,7 @@ def time_accept_sampled(w, da, stream, sv, calls=20):
                                ws_bytes, stream=sh)
     for _ in range(LEG_WARMUP):        # the GPU idled during input generation: clocks ramp up
         call()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(calls):
         call()
@@ -198,7 +248,7 @@ def time_draft_signals(w, stream, sv, calls=20):
                               stream=sh)
     for _ in range(LEG_WARMUP):        # the GPU idled during input generation: clocks ramp up
         call()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(calls):
         call()
@@ -246,7 +296,7 @@ def time_tree(w, da, p, ws, ws_bytes, out, stream, sv, calls=20):
     for name, fn in (("attn", attn), ("accept", acc)):
         for _ in range(LEG_WARMUP):    # the GPU idled during input generation: clocks ramp up
             fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev = [TimingEvent() for _ in range(2)]
         ev[0].record(stream)
         for _ in range(calls):
             fn()
@@ -268,7 +318,7 @@ def measure_ceilings(stream, sv):
     sh = stream.cuda_stream
 
     def best_us(fn, reps=5):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        ev = [TimingEvent() for _ in range(2 * reps)]
         fn()                                        # first launch: code load
         for r in range(reps):
             ev[2 * r].record(stream)
@@ -355,7 +405,7 @@ def tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs):
                 call()
             best = float("inf")
             for _ in range(3):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = TimingEvent(), TimingEvent()
                 e0.record(stream)
                 for _ in range(10):
                     call()
@@ -447,9 +497,10 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    # Two event records per timed step, around the attention call: a record
-    # costs ~6 us of stream time here, so the acceptance call is timed from the
-    # second one to the next step's first (the last step: to the stop event).
+    # Two event records per timed step, around the attention call (each adds
+    # stream time, ~1.5 us with TimingEvent), so the acceptance call is timed
+    # from the second one to the next step's first (the last step: to the stop
+    # event) rather than between two records of its own.
     def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -464,8 +515,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
+    start, stop = TimingEvent(), TimingEvent()
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
