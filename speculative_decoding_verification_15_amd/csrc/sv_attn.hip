@@ -683,6 +683,17 @@ __device__ __forceinline__ void dma_to_lds16(const void* src, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// 4 bytes per active lane from global memory into LDS (global_load_lds_dword:
+// lane i's dword lands at lds + 4 i), with the same M0 contract as
+// dma_to_lds16.  Counted by vmcnt like the tile loads, so it is ordered with
+// them by the same waits.
+__device__ __forceinline__ void dma_to_lds4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
 // N such loads of consecutive 1 KB pieces: piece j of the wave's source (src +
 // 1024 j + 16 i for lane i) lands at lds + 1024 j + 16 i.  One M0 value serves
 // all of them: the instruction's immediate offset is added to both the global
@@ -1647,8 +1658,8 @@ void sv_attn_streamk_f8(AttnArgs a) {
   static_assert(NS >= 4, "the ring holds the computed tile, the next one and two in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   // per stage: K scale, log2 of the V scale and its reciprocal of blocks 0..3
-  __shared__ f32x4 s_scale[NS][3];
-  __shared__ float s_sink[kLdsThreads];       // scale stores by lanes other than 0
+  // per stage: K and V scale of block w at [2 w] and [2 w + 1], DMA'd by wave w
+  __shared__ __attribute__((aligned(16))) float s_sc[NS][8];
   static_assert((kStreamMaxBatch + 1 + 4) * 4 <= NS * STAGE, "prefix table fits");
   int* s_pref = reinterpret_cast<int*>(smem);
   int* s_wsum = s_pref + kStreamMaxBatch + 1;
@@ -1672,8 +1683,8 @@ void sv_attn_streamk_f8(AttnArgs a) {
   const int lane = tid % kWave;
   const int ql = lane & 31, hh = lane >> 5;
   const uint32_t blk_stride32 = (uint32_t)a.H_kv * BLK;   // below 2^32 (the planner checks)
-  const SV_CONST float* ksc = (const SV_CONST float*)a.k_scale;
-  const SV_CONST float* vsc = (const SV_CONST float*)a.v_scale;
+  const float* ksc = a.k_scale;
+  const float* vsc = a.v_scale;
 
   // Operand offsets of this lane inside a stage: K row ql of a 32-key half is
   // key key_of_row(ql) (block ql / 16 of the half, slot key_of_row(ql) % 16),
@@ -1694,9 +1705,14 @@ void sv_attn_streamk_f8(AttnArgs a) {
   constexpr int VPW = BLK / 1024;             // V pieces per wave (4 waves x VPW = 4 BLK / 1 KB)
   const int vb_lane = (lane >> 3) & 3;        // block of this lane's V piece rows
   const int vd_lane = (lane & 7) + 8 * (lane >> 5);   // dim within a piece's 16 dims
-  // Loads of one tile into stage `stage`; this wave's block's K and V scales
-  // come back (scalar loads, stored to LDS for all waves an iteration later).
-  auto issue = [&](const Cursor& c, const i32x4& raw, int stage, float& sk, float& sv) {
+  // Loads of one tile into stage `stage`, then this wave's block's K and V
+  // scales into s_sc[stage] (lanes 0 and 1).  The scales are DMA'd rather than
+  // read with scalar loads: the blocks are scattered, so those loads missed
+  // the caches, and every LDS wait of the iteration (one counter covers LDS
+  // and scalar loads) then waited for them as well.  As vector-memory loads
+  // they complete in order with the tile's own and are covered by the ring's
+  // waits.
+  auto issue = [&](const Cursor& c, const i32x4& raw, int stage) {
     const uint32_t last = (uint32_t)(a.num_blocks - 1);
     const uint32_t pw = (uint32_t)min(max(raw[wave], 0), (int)last);
     const uint32_t head = (uint32_t)(c.kvh * BLK);
@@ -1712,18 +1728,7 @@ void sv_attn_streamk_f8(AttnArgs a) {
       dma_to_lds16<NT>(vsrc + (16 * piece + vd_lane) * 16, l + 4 * BLK + piece * 1024);
     }
     const uint32_t si = pw * (uint32_t)a.H_kv + (uint32_t)c.kvh;
-    sk = ksc[si];
-    sv = vsc[si];
-  };
-  // This wave's block factors of a tile into s_scale[stage][.][wave]: one
-  // store per lane (lane 0 to the slot, the others to sinks), no branch.
-  auto put_scale = [&](int stage, float sk, float sv) {
-    float* d0 = lane == 0 ? reinterpret_cast<float*>(&s_scale[stage][0]) + wave : &s_sink[tid];
-    float* d1 = lane == 0 ? reinterpret_cast<float*>(&s_scale[stage][1]) + wave : &s_sink[tid];
-    float* d2 = lane == 0 ? reinterpret_cast<float*>(&s_scale[stage][2]) + wave : &s_sink[tid];
-    *d0 = sk;
-    *d1 = __builtin_amdgcn_logf(sv);
-    *d2 = __builtin_amdgcn_rcpf(sv);
+    if (lane < 2) dma_to_lds4((lane == 0 ? ksc : vsc) + si, lds_addr(&s_sc[stage][2 * wave]));
   };
 
   Cursor ci = cursor_at(a, s_pref, g0);      // next tile to load (index gi)
@@ -1749,13 +1754,9 @@ void sv_attn_streamk_f8(AttnArgs a) {
 
   int gi = g0;
   i32x4 ent = entry(ci);
-  float sk_next = 0.f, sv_next = 1.f;          // scales of the tile issued last
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k) {         // past the range: the last tile again
-    float sk, sv;
-    issue(ci, ent, k, sk, sv);
-    if (k < NS - 2) put_scale(k, sk, sv);
-    else { sk_next = sk; sv_next = sv; }
+    issue(ci, ent, k);
     if (gi + 1 < g1) cursor_next<KEYS>(a, ci);
     ++gi;
     ent = entry(ci);
@@ -1770,9 +1771,10 @@ void sv_attn_streamk_f8(AttnArgs a) {
   i32x8 phi = {}, plo = {};                    // probability operands (hi, lo) of the last tile
   for (int g = g0; g < g1; ++g) {
     const unsigned t = (unsigned)(g - g0);
-    // This wave's loads of tiles g and g + 1 landed (tile g + 2's may not
-    // have: loads retire in issue order) ...
-    wait_vmcnt<(NS - 3) * 2 * LPB>();
+    // This wave's loads of tiles g and g + 1 landed (tile g + 2's -- K, V and
+    // the scales, 2 LPB + 1 loads -- may not have: loads retire in issue
+    // order) ...
+    wait_vmcnt<(NS - 3) * (2 * LPB + 1)>();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();              // ... and every other wave's; stage g - 1 is free
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -1789,8 +1791,7 @@ void sv_attn_streamk_f8(AttnArgs a) {
       have_xn = false;
     }
     // the scales of the tile issued last iteration, then this iteration's load
-    put_scale((t + NS - 2) % NS, sk_next, sv_next);
-    issue(ci, ent, (t + NS - 1) % NS, sk_next, sv_next);   // refills the stage of tile g - 1
+    issue(ci, ent, (t + NS - 1) % NS);        // refills the stage of tile g - 1
     if (gi + 1 < g1) cursor_next<KEYS>(a, ci);
     ++gi;
     ent = entry(ci);
@@ -1822,10 +1823,13 @@ void sv_attn_streamk_f8(AttnArgs a) {
       const uint8_t* nstage = smem + ((t + 1) % NS) * STAGE;
       xn[0] = sk8_scores<HD>(nstage, k_lds, 0, qhi, qlo);
       xn[1] = sk8_scores<HD>(nstage, k_lds, 1, qhi, qlo);
-      const f32x4 skv = s_scale[t % NS][0], lvv = s_scale[t % NS][1], rvv = s_scale[t % NS][2];
-      const float cb[4] = {c_row * skv[0], c_row * skv[1], c_row * skv[2], c_row * skv[3]};
-      const float lv[4] = {lvv[0], lvv[1], lvv[2], lvv[3]};
-      const float rv[4] = {rvv[0], rvv[1], rvv[2], rvv[3]};
+      const f32x4 sc01 = *reinterpret_cast<const f32x4*>(&s_sc[t % NS][0]);
+      const f32x4 sc23 = *reinterpret_cast<const f32x4*>(&s_sc[t % NS][4]);
+      const float cb[4] = {c_row * sc01[0], c_row * sc01[2], c_row * sc23[0], c_row * sc23[2]};
+      const float lv[4] = {__builtin_amdgcn_logf(sc01[1]), __builtin_amdgcn_logf(sc01[3]),
+                           __builtin_amdgcn_logf(sc23[1]), __builtin_amdgcn_logf(sc23[3])};
+      const float rv[4] = {__builtin_amdgcn_rcpf(sc01[1]), __builtin_amdgcn_rcpf(sc01[3]),
+                           __builtin_amdgcn_rcpf(sc23[1]), __builtin_amdgcn_rcpf(sc23[3])};
       float alpha;
       int sb;
       const bool rescale = softmax_tile8(x, cb, lv, rv, m_ref, l_run, alpha, phi, plo, sb);
