@@ -40,7 +40,8 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0
 METRIC = "verified tokens/sec + KV HBM GB/s (% peak) at Llama-70B-like GQA, D=15"
 KERNEL_SOURCES = ("speculative_decoding_verification_15_amd/csrc/sv_attn.hip",
                   "speculative_decoding_verification_15_amd/csrc/sv_device.h",
-                  "speculative_decoding_verification_15_amd/csrc/sv_attn_plan.h")
+                  "speculative_decoding_verification_15_amd/csrc/sv_attn_plan.h",
+                  "speculative_decoding_verification_15_amd/csrc/sv_plan.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sv_attn.md")
 
 
@@ -383,8 +384,10 @@ def cpu_baseline(w, inp, plan, draft, budget_s=15.0):
 
 def tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs):
     """spec_verify_attn alone on the tile-boundary shapes (B=8, T=16384, bf16;
-    H_kv = 8 or 1, D in SWEEP_D): 100 untimed calls, then the best of three runs
-    of 10 calls timed with HIP events on the launch stream."""
+    H_kv = 8 or 1, D in SWEEP_D): untimed calls for at least 100 calls and 80 ms
+    (the GPU idles while each shape's inputs are generated, and its clock dips
+    for several ms after it becomes busy again), then the best of three runs of
+    10 calls timed with HIP events on the launch stream."""
     import torch
     from workloads import SWEEP_D, tile_sweep
     stream = torch.cuda.current_stream()
@@ -401,7 +404,15 @@ def tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs):
             def call():
                 sv.spec_verify_attn(p, d.q, d.k, d.v, d.ks, d.vs, d.bt, d.kl, out, ws, plan_ws,
                                     stream=stream.cuda_stream)
-            for _ in range(LEG_WARMUP):
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record(stream)
+            for _ in range(10):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            first_ms = e0.elapsed_time(e1) / 10
+            n_warm = max(LEG_WARMUP - 10, int(80.0 / first_ms))
+            for _ in range(n_warm):
                 call()
             best = float("inf")
             for _ in range(3):
@@ -416,6 +427,7 @@ def tile_sweep_leg(sv, DeviceAttn, attn_params, make_attn_inputs):
             fl = attn_algorithmic_flops(inp)
             m_pad = -(-w.M // 128) * 128              # rows rounded to 128-row tiles
             print(json.dumps({"tile_sweep": w.name, "M": w.M, "M_pad": m_pad, "us": round(best, 1),
+                              "calls": 10 + n_warm + 30,
                               "TFLOPs_padded": round(fl * m_pad / w.M / (best * 1e-6) / 1e12, 1),
                               "kv_GBps": round(kv / (best * 1e-6) / 1e9, 1),
                               "TFLOPs": round(fl / (best * 1e-6) / 1e12, 1),

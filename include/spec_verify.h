@@ -143,7 +143,7 @@ sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes
  * H_kv*hd*32 < 2^31 (bytes of one physical block of a bf16 cache, all KV
  * heads); num_blocks*H_kv < 2^32 (entries of a scale array); for B <= 2048,
  * B*H_kv*ceil(M/128)*ceil(max_kv_len/32) < 2^31 (32-key tiles of the whole
- * batch, M = G*R rows per KV head; 256 rows per tile when 128 < M <= 256).
+ * batch, M = G*R rows per KV head; 256 rows per tile when 128 < M < 256).
  *
  * Device preconditions: R <= kv_lens[b] <= max_kv_len; block_table[b][j] in
  * [0, num_blocks) for j < ceil(kv_lens[b] / 16).  The other entries of the

@@ -1154,8 +1154,8 @@ __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
 
 // NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
 // read by that unit alone (one row tile per KV head).  WAVES = 4 (units of 128
-// rows, two workgroups per CU) or 8 (units of 256 rows, one per CU), so that
-// up to 256 rows of one KV head stream its K and V once.
+// rows, two workgroups per CU) or 8 (units of 256 rows, one per CU, for 129 ..
+// 255 rows per KV head), so that those rows stream their K and V once.
 // TREE: draft-tree verification (ancestor masks instead of the causal chain).
 // Work-list range of this workgroup.  Workgroups go to the 8 XCDs in turn
 // (workgroup i to XCD i % 8), each XCD with its own L2.  When a KV head's rows

@@ -13,15 +13,18 @@ void plan_attention(AttnPlan& p, int split_request) {
   // Batches up to kStreamMaxBatch go through the stream-K ring whatever M is:
   // waves beyond M still move their share of every tile (the K/V stream, not
   // the MFMA work, sets the pace when few rows share a KV head).  bf16 units
-  // hold 128 rows (4 waves, two workgroups per CU) or, for 129 .. 256 rows per
+  // hold 128 rows (4 waves, two workgroups per CU) or, for 129 .. 255 rows per
   // KV head, 256 rows (8 waves, one workgroup per CU), so that those rows
-  // stream their K and V once instead of twice.  Beyond 256 rows (MQA-like
-  // heads) the row tiles of a KV head share its K/V through L2 and two 4-wave
-  // workgroups per CU hide latency better (measured); e4m3 units hold 128.
+  // stream their K and V once instead of twice.  From 256 rows on, the 128-row
+  // units of a KV head run on one XCD at the same time (ranges numbered XCD by
+  // XCD) and share its K/V through L2, and two 4-wave workgroups per CU hide
+  // latency better (measured); below 256 the second unit would be partly
+  // empty, and stream-K, which balances tiles, would give its light ranges the
+  // same share.  e4m3 units hold 128.
   p.streamk = p.B <= kStreamMaxBatch;
   const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
   if (p.streamk)
-    p.waves = (!p.fp8 && p.M > kStreamRows && p.M <= 2 * kStreamRows) ? 8 : 4;
+    p.waves = (!p.fp8 && p.M > kStreamRows && p.M < 2 * kStreamRows) ? 8 : 4;
   else
     p.waves = waves_needed > 2 ? 4 : waves_needed;
   p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);
