@@ -1157,16 +1157,23 @@ __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
 // rows, two workgroups per CU) or 8 (units of 256 rows, one per CU, for 129 ..
 // 255 rows per KV head), so that those rows stream their K and V once.
 // TREE: draft-tree verification (ancestor masks instead of the causal chain).
-// Work-list range of this workgroup.  Workgroups go to the 8 XCDs in turn
-// (workgroup i to XCD i % 8), each XCD with its own L2.  When a KV head's rows
-// span several units (m_tiles > 1), consecutive units stream the same K/V
-// tiles at the same time, so the ranges are numbered XCD by XCD: consecutive
-// ranges run on one XCD and share its L2 (MQA with 2048 rows: 153-156 against
-// 161-164 us).  With one unit per KV head consecutive ranges share no K/V, and
-// the plain order is kept.
-__device__ __forceinline__ int sk_range(const AttnArgs& a) {
+// Work-list range of this workgroup (W tiles in ranges of Wp).  Workgroups go
+// to the 8 XCDs in turn (workgroup i to XCD i % 8), each XCD with its own L2.
+// When a KV head's rows span several units (m_tiles > 1), consecutive units
+// stream the same K/V tiles at the same time, so the ranges that hold tiles
+// are dealt out XCD by XCD, ceil(nr / 8) consecutive ones to each: they run on
+// one XCD and share its L2 (MQA with 2048 rows: 153-156 against 161-164 us),
+// and every XCD gets a share however few ranges there are.  Workgroups left
+// over get range nr, past the last tile.  With one unit per KV head
+// consecutive ranges share no K/V, and the plain order is kept.
+__device__ __forceinline__ int sk_range(const AttnArgs& a, int W, int Wp) {
   const int n = (int)gridDim.x, i = (int)blockIdx.x;
-  return (a.m_tiles > 1 && n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
+  if (a.m_tiles <= 1 || n % 8 != 0) return i;
+  const int nr = Wp > 0 ? (W + Wp - 1) / Wp : 0;   // ranges holding tiles (<= n)
+  const int per = (nr + 7) / 8;                // ranges per XCD
+  const int k = i / 8;
+  const int r = (i % 8) * per + k;
+  return k < per && r < nr ? r : nr;
 }
 
 template <int HD, int NS, int WPE, bool NT, int WAVES, bool TREE>
@@ -1201,7 +1208,8 @@ void sv_attn_streamk(AttnArgs a) {
       a.sk_meta[1] = Wp;
     }
   }
-  const int g0 = sk_range(a) * Wp;
+  const int rng = sk_range(a, W, Wp);
+  const int g0 = rng * Wp;
   const int g1 = min(g0 + Wp, W);
   if (g0 >= g1) return;                       // whole workgroup, after the last barrier use
 
@@ -1360,7 +1368,7 @@ void sv_attn_streamk(AttnArgs a) {
       if (active)
         sk_segment_end<HD>(a, r, o, m_ref, l_run,
                            cc.tile == cc.T - 1 && seg_start == g - cc.tile,
-                           sk_range(a) * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
+                           rng * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
     if (g + 1 < g1) cursor_next<kSkKeys>(a, cc);
   }
@@ -1687,7 +1695,8 @@ void sv_attn_streamk_f8(AttnArgs a) {
       a.sk_meta[1] = Wp;
     }
   }
-  const int g0 = sk_range(a) * Wp;
+  const int rng = sk_range(a, W, Wp);
+  const int g0 = rng * Wp;
   const int g1 = min(g0 + Wp, W);
   if (g0 >= g1) return;                       // whole workgroup, after the last barrier use
 
@@ -1862,7 +1871,7 @@ void sv_attn_streamk_f8(AttnArgs a) {
       if (active)
         sk_segment_end<HD>(a, r, o, m_ref, l_run,
                            cc.tile == cc.T - 1 && seg_start == g - cc.tile,
-                           sk_range(a) * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
+                           rng * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
     }
     if (g + 1 < g1) cursor_next<KEYS>(a, cc);
   }
