@@ -1152,11 +1152,6 @@ __device__ __forceinline__ void sk_segment_end(const AttnArgs& a, RowCtx& r,
                                 a.ws_ml + (size_t)slot * a.sk_rows + wave * kRowsPerWave + lane);
 }
 
-// NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
-// read by that unit alone (one row tile per KV head).  WAVES = 4 (units of 128
-// rows, two workgroups per CU) or 8 (units of 256 rows, one per CU, for 129 ..
-// 255 rows per KV head), so that those rows stream their K and V once.
-// TREE: draft-tree verification (ancestor masks instead of the causal chain).
 // Work-list range of this workgroup (W tiles in ranges of Wp).  Workgroups go
 // to the 8 XCDs in turn (workgroup i to XCD i % 8), each XCD with its own L2.
 // When a KV head's rows span several units (m_tiles > 1), consecutive units
@@ -1176,6 +1171,11 @@ __device__ __forceinline__ int sk_range(const AttnArgs& a, int W, int Wp) {
   return k < per && r < nr ? r : nr;
 }
 
+// NT: K/V loads are non-temporal, for row tilings where each unit's K and V are
+// read by that unit alone (one row tile per KV head).  WAVES = 4 (units of 128
+// rows, two workgroups per CU) or 8 (units of 256 rows, one per CU, for 129 ..
+// 255 rows per KV head), so that those rows stream their K and V once.
+// TREE: draft-tree verification (ancestor masks instead of the causal chain).
 template <int HD, int NS, int WPE, bool NT, int WAVES, bool TREE>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64),
                           amdgpu_waves_per_eu(WPE, WPE)))
@@ -1677,7 +1677,6 @@ void sv_attn_streamk_f8(AttnArgs a) {
   constexpr int LPB = T8::kLoads;
   static_assert(NS >= 4, "the ring holds the computed tile, the next one and two in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-  // per stage: K scale, log2 of the V scale and its reciprocal of blocks 0..3
   // per stage: K and V scale of block w at [2 w] and [2 w + 1], DMA'd by wave w
   __shared__ __attribute__((aligned(16))) float s_sc[NS][8];
   static_assert((kStreamMaxBatch + 1 + 4) * 4 <= NS * STAGE, "prefix table fits");
@@ -1811,7 +1810,6 @@ void sv_attn_streamk_f8(AttnArgs a) {
       l_run = 0.f;
       have_xn = false;
     }
-    // the scales of the tile issued last iteration, then this iteration's load
     issue(ci, ent, (t + NS - 1) % NS);        // refills the stage of tile g - 1
     if (gi + 1 < g1) cursor_next<KEYS>(a, ci);
     ++gi;
