@@ -96,9 +96,14 @@ class TimingEvent:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernels' code (comments and blank space dropped,
+    so that a comment edit does not orphan the counter summaries keyed to it)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        src = open(os.path.join(ROOT, p)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
