@@ -85,6 +85,21 @@ def test_attention_tile_sweep_sampled(D, mqa):
     _full_size(tile_sweep(D, mqa))
 
 
+# e4m3 caches with several 128-row units per KV head, whose stream-K ranges are
+# dealt out XCD by XCD (G (1 + D) = 256 and 512 rows; few tiles, so most
+# workgroups get no range).
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("H_q,H_kv,D", [(32, 2, 15), (64, 1, 7)])
+def test_fp8_several_row_units_per_kv_head(H_q, H_kv, D, split):
+    w = MINI["mini_fp8_d15"].replace(name=f"mini_fp8_g{H_q // H_kv}_d{D}", H_q=H_q, H_kv=H_kv,
+                                     D=D, T_range=(100, 1500))
+    assert w.M > 128
+    inp = make_attn_inputs(w)
+    gpu = run_attention(inp, split_tokens=split)
+    assert np.isfinite(gpu).all()
+    check(gpu, oracle_for(inp), f"{w.name}/split={split}")
+
+
 def test_tiny_contiguous_exact_shape():
     inp = make_attn_inputs(TINY)
     assert inp.kv_lens.tolist() == [260] and (inp.block_table[0, :17] == np.arange(17)).all()
