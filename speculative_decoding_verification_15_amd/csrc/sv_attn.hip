@@ -43,6 +43,8 @@
 #include "sv_device.h"
 #include "sv_attn_plan.h"
 
+#include <type_traits>
+
 namespace sv {
 
 struct AttnArgs {
@@ -1268,7 +1270,6 @@ void sv_attn_streamk(AttnArgs a) {
   };
   RowCtx r, rn;                                // segment of tile g; the next segment
   bool active = seg_ctx(cc, r), active_n = false;
-  int seg_start = g0;
   bf16x8 qop[KS], qn[KS];
   if (active) load_q<HD, false>(a, r, qop);
   wait_vmcnt<0>();                             // Q before the ring's loads, waited once
@@ -1283,94 +1284,211 @@ void sv_attn_streamk(AttnArgs a) {
     ent = entry(ci);
   }
 
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  f32x16 xn;                                   // scores of tile g + 1, when have_xn
-  bool have_xn = false;
-  float m_ref = kNoMax, l_run = 0.f;
-  for (int g = g0; g < g1; ++g) {
-    const unsigned t = (unsigned)(g - g0);    // unsigned: stage indices are cheap remainders
-    // This wave's loads of tiles g and g + 1 landed: loads retire in issue
-    // order, so at most tile g + 2's loads (and stores issued after them) are
-    // still counted.
-    wait_vmcnt<(NS - 3) * LPW>();
-    __builtin_amdgcn_s_barrier();              // ... and every other wave's
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  // Two forms of the tile loop, chosen by measurement (outputs are bit-identical):
+  // 8-wave units (129 .. 255 rows per KV head) run a loop over the range's segments with
+  // an inner loop over their tiles, so that the per-tile path carries no segment tests
+  // (gqa8 D = 16: 151 -> 138 us); 4-wave units keep one loop over tiles with the tests
+  // inline, which measured 1-2% faster for them (70B-like 375 against 379-383 us).
+  if constexpr (WAVES == 8) {
+    f32x16 o[DB];
+    f32x16 xn;                                   // scores of the next tile, when have_xn
+    bool have_xn = false;
+    float m_ref = kNoMax, l_run = 0.f;
+    unsigned t = 0;                              // tiles computed so far (unsigned: stage
+                                                 // indices are cheap remainders)
+    int g = g0;                                  // work-list index of the tile being computed
 
-    if (g != g0 && cc.tile == 0) {             // a new segment, prepared one tile ago
-      seg_start = g;
-      r = rn;
-      active = active_n;
-      const bf16x8 z = {};
+    // One tile of the current segment, unit tile tt.  MASKED: the tile reaches
+    // past some row's last visible key (key P + pos), which also covers the
+    // sequence's last tile (keys past L) and the unit's last tile, where the
+    // next segment is prepared; every other tile of a segment takes the plain
+    // path, with none of those tests.
+    auto step = [&](const int tt, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      // This wave's loads of tiles g and g + 1 landed: loads retire in issue
+      // order, so at most tile g + 2's loads (and stores issued after them) are
+      // still counted.
+      wait_vmcnt<(NS - 3) * LPW>();
+      __builtin_amdgcn_s_barrier();              // ... and every other wave's
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      if (MASKED && tt + 1 == cc.T && g + 1 < g1) {
+        // The next tile starts a segment: its row context and Q are loaded now,
+        // ahead of this tile's ring loads, so that using them next tile waits
+        // for nothing issued later.
+        Cursor cn = cc;
+        cn.tile = tt;
+        cursor_next<kSkKeys>(a, cn);
+        active_n = seg_ctx(cn, rn);
+        if (active_n) load_q_raw<HD>(a, rn, qn);
+      }
+      issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
+      if (gi + 1 < g1) cursor_next<kSkKeys>(a, ci);
+      ++gi;
+      ent = entry(ci);
+
+      const int kt = tt * kSkKeys;
+      uint8_t* stage = smem + (t % NS) * STAGE;
+      if (MASKED && kt + kSkKeys > r.L) {        // the sequence's last tile (same for all waves)
+        sk_zero_v_tail<HD>(stage, kt, r.L);
+        __syncthreads();
+      }
+      if (active) {
+        // Software pipeline within the wave: the scores of tile g + 1 are
+        // computed (MFMA) while the softmax of tile g runs (VALU); they are kept
+        // when tile g + 1 continues this segment, which has the same Q.
+        f32x16 x = have_xn ? xn : sk_scores<HD>(stage, k_lds, qop);
+        if constexpr (MASKED) {
+          if constexpr (TREE) sk_mask_tree(x, r, kt, a);
+          else sk_mask(x, r, kt);
+        }
+        xn = sk_scores<HD>(smem + ((t + 1) % NS) * STAGE, k_lds, qop);
+        bf16x8 vop[2][DB];
+        sk_read_v<HD>(stage, v_lds, vop);
+        float alpha;
+        bf16x8 p[2];
+        const bool rescale = softmax_sub_sk(x, a.c, m_ref, l_run, alpha, p[0], p[1]);
+        // Keep the probabilities and V operands in this block (ahead of the
+        // rescale branch), and interleave: the next tile's K reads and this
+        // tile's V reads first, then each of the next tile's score MFMAs
+        // followed by a share of this tile's softmax VALU work.
+        asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
+        __builtin_amdgcn_sched_group_barrier(0x100, KS + 2 * DB, 0);  // DS reads
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // ten VALU
+        }
+        if (rescale) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+        sk_pv<HD>(vop, p, o);
+      }
+      have_xn = true;                            // the next tile of this segment has it
+      ++g;
+      ++t;
+    };
+
+    // Segments: the tiles of one unit inside this range, [cc.tile, cc.tile + n).
+    // A segment ends at its unit's last tile or at the range's end.
+    for (;;) {
+      const int seg_start = g;
+      const int tt0 = cc.tile;
+      const int n = min(g1 - g, cc.T - tt0);
+      // Tiles whose 32 keys every row of the unit sees (32 tt + 31 <= P): plain.
+      const int n_plain = min(max(max(r.P + 1, 0) / kSkKeys - tt0, 0), n);
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = f32x16{};
       m_ref = kNoMax;
       l_run = 0.f;
       have_xn = false;
-    }
-    // The next tile starts a segment: its row context and Q are loaded now,
-    // ahead of this tile's ring loads, so that using them next tile waits for
-    // nothing issued later.
-    if (g + 1 < g1 && cc.tile + 1 == cc.T) {
-      Cursor cn = cc;
-      cursor_next<kSkKeys>(a, cn);
-      active_n = seg_ctx(cn, rn);
-      if (active_n) load_q_raw<HD>(a, rn, qn);
-    }
-    issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
-    if (gi + 1 < g1) cursor_next<kSkKeys>(a, ci);
-    ++gi;
-    ent = entry(ci);
-
-    const int kt = cc.tile * kSkKeys;
-    uint8_t* stage = smem + (t % NS) * STAGE;
-    if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
-      sk_zero_v_tail<HD>(stage, kt, r.L);
-      __syncthreads();
-    }
-    if (active) {
-      // Software pipeline within the wave: the scores of tile g + 1 are
-      // computed (MFMA) while the softmax of tile g runs (VALU); they are kept
-      // when tile g + 1 continues this segment, which has the same Q.
-      f32x16 x = have_xn ? xn : sk_scores<HD>(stage, k_lds, qop);
-      if (kt + kSkKeys - 1 > r.P) {            // unless every key is visible to every row
-        if constexpr (TREE) sk_mask_tree(x, r, kt, a);
-        else sk_mask(x, r, kt);
-      }
-      xn = sk_scores<HD>(smem + ((t + 1) % NS) * STAGE, k_lds, qop);
-      bf16x8 vop[2][DB];
-      sk_read_v<HD>(stage, v_lds, vop);
-      float alpha;
-      bf16x8 p[2];
-      const bool rescale = softmax_sub_sk(x, a.c, m_ref, l_run, alpha, p[0], p[1]);
-      // Keep the probabilities and V operands in this block (ahead of the
-      // rescale branch), and interleave: the next tile's K reads and this
-      // tile's V reads first, then each of the next tile's score MFMAs
-      // followed by a share of this tile's softmax VALU work.
-      asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
-      __builtin_amdgcn_sched_group_barrier(0x100, KS + 2 * DB, 0);  // DS reads
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // ten VALU
-      }
-      if (rescale) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      }
-      sk_pv<HD>(vop, p, o);
-    }
-    have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
-    if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
+      for (int i = 0; i < n_plain; ++i) step(tt0 + i, std::false_type{});
+      for (int i = n_plain; i < n; ++i) step(tt0 + i, std::true_type{});
       if (active)
-        sk_segment_end<HD>(a, r, o, m_ref, l_run,
-                           cc.tile == cc.T - 1 && seg_start == g - cc.tile,
+        sk_segment_end<HD>(a, r, o, m_ref, l_run, tt0 == 0 && tt0 + n == cc.T,
                            rng * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
+      if (g >= g1) break;
+      // the next segment starts at tile 0 of the next unit, prepared during
+      // this segment's last tile
+      cc.tile = tt0 + n - 1;
+      cursor_next<kSkKeys>(a, cc);
+      r = rn;
+      active = active_n;
+      const bf16x8 z = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
     }
-    if (g + 1 < g1) cursor_next<kSkKeys>(a, cc);
+  } else {
+    int seg_start = g0;
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    f32x16 xn;                                   // scores of tile g + 1, when have_xn
+    bool have_xn = false;
+    float m_ref = kNoMax, l_run = 0.f;
+    for (int g = g0; g < g1; ++g) {
+      const unsigned t = (unsigned)(g - g0);    // unsigned: stage indices are cheap remainders
+      // This wave's loads of tiles g and g + 1 landed: loads retire in issue
+      // order, so at most tile g + 2's loads (and stores issued after them) are
+      // still counted.
+      wait_vmcnt<(NS - 3) * LPW>();
+      __builtin_amdgcn_s_barrier();              // ... and every other wave's
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+      if (g != g0 && cc.tile == 0) {             // a new segment, prepared one tile ago
+        seg_start = g;
+        r = rn;
+        active = active_n;
+        const bf16x8 z = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = r.row_ok ? qn[ks] : z;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+        m_ref = kNoMax;
+        l_run = 0.f;
+        have_xn = false;
+      }
+      // The next tile starts a segment: its row context and Q are loaded now,
+      // ahead of this tile's ring loads, so that using them next tile waits for
+      // nothing issued later.
+      if (g + 1 < g1 && cc.tile + 1 == cc.T) {
+        Cursor cn = cc;
+        cursor_next<kSkKeys>(a, cn);
+        active_n = seg_ctx(cn, rn);
+        if (active_n) load_q_raw<HD>(a, rn, qn);
+      }
+      issue(ci, ent, (t + NS - 1) % NS);         // refills the stage freed by tile g - 1
+      if (gi + 1 < g1) cursor_next<kSkKeys>(a, ci);
+      ++gi;
+      ent = entry(ci);
+
+      const int kt = cc.tile * kSkKeys;
+      uint8_t* stage = smem + (t % NS) * STAGE;
+      if (kt + kSkKeys > r.L) {                  // the sequence's last tile (same for all waves)
+        sk_zero_v_tail<HD>(stage, kt, r.L);
+        __syncthreads();
+      }
+      if (active) {
+        // Software pipeline within the wave: the scores of tile g + 1 are
+        // computed (MFMA) while the softmax of tile g runs (VALU); they are kept
+        // when tile g + 1 continues this segment, which has the same Q.
+        f32x16 x = have_xn ? xn : sk_scores<HD>(stage, k_lds, qop);
+        if (kt + kSkKeys - 1 > r.P) {            // unless every key is visible to every row
+          if constexpr (TREE) sk_mask_tree(x, r, kt, a);
+          else sk_mask(x, r, kt);
+        }
+        xn = sk_scores<HD>(smem + ((t + 1) % NS) * STAGE, k_lds, qop);
+        bf16x8 vop[2][DB];
+        sk_read_v<HD>(stage, v_lds, vop);
+        float alpha;
+        bf16x8 p[2];
+        const bool rescale = softmax_sub_sk(x, a.c, m_ref, l_run, alpha, p[0], p[1]);
+        // Keep the probabilities and V operands in this block (ahead of the
+        // rescale branch), and interleave: the next tile's K reads and this
+        // tile's V reads first, then each of the next tile's score MFMAs
+        // followed by a share of this tile's softmax VALU work.
+        asm volatile("" : : "v"(p[0]), "v"(p[1]), "v"(l_run));
+        __builtin_amdgcn_sched_group_barrier(0x100, KS + 2 * DB, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);         // ten VALU
+        }
+        if (rescale) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+        sk_pv<HD>(vop, p, o);
+      }
+      have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
+      if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
+        if (active)
+          sk_segment_end<HD>(a, r, o, m_ref, l_run,
+                             cc.tile == cc.T - 1 && seg_start == g - cc.tile,
+                             rng * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
+      }
+      if (g + 1 < g1) cursor_next<kSkKeys>(a, cc);
+    }
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
