@@ -1882,7 +1882,6 @@ void sv_attn_streamk_f8(AttnArgs a) {
   };
   RowCtx r;
   bool active = seg_ctx(cc, r);
-  int seg_start = g0;
   i32x8 qhi[KB], qlo[KB];
   float c_row = a.c;
   uint64_t anc = 0;
@@ -1901,14 +1900,17 @@ void sv_attn_streamk_f8(AttnArgs a) {
   }
 
   f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  f32x16 xn[2];                                // scores of tile g + 1, when have_xn
+  f32x16 xn[2];                                // scores of the next tile, when have_xn
   bool have_xn = false;
   float m_ref = kNoMax, l_run = 0.f;
   i32x8 phi = {}, plo = {};                    // probability operands (hi, lo) of the last tile
-  for (int g = g0; g < g1; ++g) {
-    const unsigned t = (unsigned)(g - g0);
+  unsigned t = 0;                              // tiles computed so far
+  int g = g0;                                  // work-list index of the tile being computed
+
+  // One tile of the current segment, unit tile tt (MASKED: the tile reaches
+  // past some row's last visible key, which covers the sequence's last tile).
+  auto step = [&](const int tt, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     // This wave's loads of tiles g and g + 1 landed (tile g + 2's -- K, V and
     // the scales, 2 LPB + 1 loads -- may not have: loads retire in issue
     // order) ...
@@ -1916,26 +1918,14 @@ void sv_attn_streamk_f8(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();              // ... and every other wave's; stage g - 1 is free
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-
-    if (g != g0 && cc.tile == 0) {             // a new segment
-      seg_start = g;
-      active = seg_ctx(cc, r);
-      if (active) load_q_e4m3<HD>(a, r, qhi, qlo, c_row);
-      if constexpr (TREE) anc = tree_masks(a)[(size_t)r.b * a.R + r.pos];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-      m_ref = kNoMax;
-      l_run = 0.f;
-      have_xn = false;
-    }
     issue(ci, ent, (t + NS - 1) % NS);        // refills the stage of tile g - 1
     if (gi + 1 < g1) cursor_next<KEYS>(a, ci);
     ++gi;
     ent = entry(ci);
 
-    const int kt = cc.tile * KEYS;
+    const int kt = tt * KEYS;
     uint8_t* stage = smem + (t % NS) * STAGE;
-    if (kt + KEYS > r.L) {                     // the sequence's last tile (same for all waves)
+    if (MASKED && kt + KEYS > r.L) {           // the sequence's last tile (same for all waves)
       sk8_zero_v_tail<HD>(stage, kt, r.L);
       __syncthreads();
     }
@@ -1948,7 +1938,7 @@ void sv_attn_streamk_f8(AttnArgs a) {
         x[0] = sk8_scores<HD>(stage, k_lds, 0, qhi, qlo);
         x[1] = sk8_scores<HD>(stage, k_lds, 1, qhi, qlo);
       }
-      if (kt + KEYS - 1 > r.P) {               // unless every key is visible to every row
+      if constexpr (MASKED) {
         if constexpr (TREE) {
           sk8_mask_tree(x[0], r, kt, 0, anc, a.R);
           sk8_mask_tree(x[1], r, kt, 1, anc, a.R);
@@ -1971,10 +1961,8 @@ void sv_attn_streamk_f8(AttnArgs a) {
       int sb;
       const bool rescale = softmax_tile8(x, cb, lv, rv, m_ref, l_run, alpha, phi, plo, sb);
       // Keep the probabilities in this block, ahead of the rescale branch.
-      // (Interleaving the next tile's score MFMAs with this softmax through
-      // schedule groups, as the bf16 kernel does, measured slower here: the
-      // two waves of a SIMD already alternate between their VALU and MFMA
-      // phases.)
+      // (Schedule groups that interleave the next tile's score MFMAs with the
+      // softmax, as in the bf16 kernel, measured slower here.)
       asm volatile("" : : "v"(phi), "v"(plo), "v"(l_run));
       if (rescale) {
 #pragma unroll
@@ -1982,14 +1970,34 @@ void sv_attn_streamk_f8(AttnArgs a) {
       }
       sk8_pv<HD>(stage, v_lds, phi, plo, sb, o);
     }
-    have_xn = g + 1 < g1 && cc.tile + 1 < cc.T;
-    if (cc.tile == cc.T - 1 || g == g1 - 1) {  // the segment ends
-      if (active)
-        sk_segment_end<HD>(a, r, o, m_ref, l_run,
-                           cc.tile == cc.T - 1 && seg_start == g - cc.tile,
-                           rng * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
-    }
-    if (g + 1 < g1) cursor_next<KEYS>(a, cc);
+    have_xn = true;
+    ++g;
+    ++t;
+  };
+
+  // Segments: the tiles of one unit inside this range; the per-tile path
+  // carries no segment tests (e4m3 long context: 333 -> 327 us, bit-identical).
+  for (;;) {
+    const int seg_start = g;
+    const int tt0 = cc.tile;
+    const int n = min(g1 - g, cc.T - tt0);
+    const int n_plain = min(max(max(r.P + 1, 0) / KEYS - tt0, 0), n);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    m_ref = kNoMax;
+    l_run = 0.f;
+    have_xn = false;
+    for (int i = 0; i < n_plain; ++i) step(tt0 + i, std::false_type{});
+    for (int i = n_plain; i < n; ++i) step(tt0 + i, std::true_type{});
+    if (active)
+      sk_segment_end<HD>(a, r, o, m_ref, l_run, tt0 == 0 && tt0 + n == cc.T,
+                         rng * 2 + (seg_start == g0 ? 0 : 1), wave, lane);
+    if (g >= g1) break;
+    cc.tile = tt0 + n - 1;
+    cursor_next<KEYS>(a, cc);
+    active = seg_ctx(cc, r);
+    if (active) load_q_e4m3<HD>(a, r, qhi, qlo, c_row);
+    if constexpr (TREE) anc = tree_masks(a)[(size_t)r.b * a.R + r.pos];
   }
   wait_vmcnt<0>();                             // drain loads issued past the range
 }
