@@ -13,18 +13,22 @@ void plan_attention(AttnPlan& p, int split_request) {
   // Batches up to kStreamMaxBatch go through the stream-K ring whatever M is:
   // waves beyond M still move their share of every tile (the K/V stream, not
   // the MFMA work, sets the pace when few rows share a KV head).  bf16 units
-  // hold 128 rows (4 waves, two workgroups per CU) or, for 129 .. 255 rows per
-  // KV head, 256 rows (8 waves, one workgroup per CU), so that those rows
-  // stream their K and V once instead of twice.  From 256 rows on, the 128-row
-  // units of a KV head run on one XCD at the same time (ranges numbered XCD by
-  // XCD) and share its K/V through L2, and two 4-wave workgroups per CU hide
-  // latency better (measured); below 256 the second unit would be partly
-  // empty, and stream-K, which balances tiles, would give its light ranges the
-  // same share.  e4m3 units hold 128.
+  // hold 256 rows (8 waves, one workgroup per CU) for 129 .. 255 rows per KV
+  // head, so that those rows stream their K and V once instead of twice, and
+  // past 256 rows whenever they pad the rows to no more than 128-row units do
+  // (M a multiple of 256, or M mod 256 above 128): the 8-wave loop (segment
+  // tests off the per-tile path) then runs faster than two 4-wave workgroups
+  // (MQA with 512, 1024, 1536 and 2048 rows: 56.0 -> 55.4, 90.8 -> 84.7, 125.1
+  // -> 117.3 and 149.2 -> 144.8 us), while 1088 rows in 256-row units
+  // measured 88.3 -> 91.5 us.  Otherwise units hold 128 rows (4 waves, two
+  // workgroups per CU), also at exactly 256 rows (MQA: 43.8 against 44.0
+  // us).  The units of a KV head run on one XCD at the same time (ranges
+  // numbered XCD by XCD) and share its K/V through L2.  e4m3 units hold 128.
   p.streamk = p.B <= kStreamMaxBatch;
   const int waves_needed = (p.M + kRowsPerWave - 1) / kRowsPerWave;
+  const bool pads_as_128 = p.M % (2 * kStreamRows) == 0 || p.M % (2 * kStreamRows) > kStreamRows;
   if (p.streamk)
-    p.waves = (!p.fp8 && p.M > kStreamRows && p.M < 2 * kStreamRows) ? 8 : 4;
+    p.waves = (!p.fp8 && p.M > kStreamRows && p.M != 2 * kStreamRows && pads_as_128) ? 8 : 4;
   else
     p.waves = waves_needed > 2 ? 4 : waves_needed;
   p.m_tiles = (p.M + kRowsPerWave * p.waves - 1) / (kRowsPerWave * p.waves);

@@ -101,8 +101,8 @@ static void attention() {
       ++g_fail;
     }
   }
-  // the 2^31 stream-K tile count
-  sv_attn_params big = attn(2048, 63, 128, 1, 64, 32768, 1 << 20, 524288);
+  // the 2^31 stream-K tile count (2048 sequences x 32 row tiles of 256 x 32768 tiles)
+  sv_attn_params big = attn(2048, 63, 128, 1, 64, 65536, 1 << 20, 1 << 20);
   EXPECT(spec_verify_attn_workspace_size(&big, &ws), SV_ERR_UNSUPPORTED);
 }
 

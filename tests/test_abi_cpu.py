@@ -543,15 +543,15 @@ def test_binding_rejects_cpu_strided_and_short_tensors():
 
 def test_streamk_tile_count_overflow_is_rejected():
     """The stream-K work list counts the batch's 32-key tiles in int32: a shape
-    with 2^31 of them is refused (here 2048 sequences x 64 row tiles of 128 x
-    16384 tiles), one tile fewer per row tile is accepted."""
+    with 2^31 of them is refused (here 2048 sequences x 32 row tiles of 256 x
+    32768 tiles), one tile fewer per row tile is accepted."""
     kw = dict(batch=2048, draft_len=63, num_q_heads=128, num_kv_heads=1, head_dim=64,
-              max_blocks_per_seq=32768, num_blocks=1 << 20, max_kv_len=524288)
+              max_blocks_per_seq=65536, num_blocks=1 << 20, max_kv_len=1 << 20)
     with pytest.raises(sv.SvError) as e:
         sv.spec_verify_attn_workspace_size(sv.make_attn_params(**kw))
     assert e.value.status == sv.SV_ERR_UNSUPPORTED
     assert "tiles" in sv.last_error()
-    kw["max_kv_len"] = 524288 - 32
+    kw["max_kv_len"] = (1 << 20) - 32
     assert sv.spec_verify_attn_workspace_size(sv.make_attn_params(**kw)) > 0
 
 
