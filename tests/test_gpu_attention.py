@@ -133,7 +133,8 @@ TAIL_REMAINDERS = [1, 5, 16, 31, 32, 33, 63, 64]
 
 
 @pytest.mark.parametrize("split", [0, 64, 1 << 20])
-@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15", "mini_gqa4_d7", "mini_mqa_d16"])
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15", "mini_gqa4_d7", "mini_mqa_d16",
+                                  "mini_mqa_d15"])
 def test_attention_dead_tail_subblocks(name, split):
     w = MINI[name]
     L = np.array([64 * (3 + i) + rem for i, rem in enumerate(TAIL_REMAINDERS)])

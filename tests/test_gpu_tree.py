@@ -55,7 +55,7 @@ def _check(gpu, ref, label):
 
 
 SHAPES = ["mini_gqa8_d15", "mini_fp8_d15", "mini_hd64_g4", "mini_mqa_d16", "mini_fp8_hd64",
-          "mini_gqa4_d7"]
+          "mini_gqa4_d7", "mini_mqa_d15"]
 
 
 @pytest.mark.parametrize("shape", ["random", "star"])
@@ -90,7 +90,7 @@ def test_tree_attention_64_nodes():
     _check(gpu, _oracle(inp, plan.parents), "edge_d63/random")
 
 
-@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15", "mini_mqa_d16"])
+@pytest.mark.parametrize("name", ["mini_gqa8_d15", "mini_fp8_d15", "mini_mqa_d16", "mini_mqa_d15"])
 def test_chain_tree_equals_chain_attention_bitwise(name):
     inp = make_attn_inputs(MINI[name])
     plan = make_tree_plan(inp.w, shape="chain")

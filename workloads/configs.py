@@ -115,6 +115,9 @@ MINI = {
                              T_range=(100, 700)),
     "mini_mqa_d3": Workload("mini_mqa_d3", 2005, B=2, H_q=64, H_kv=1, hd=128, D=3,
                             T_range=(500, 1300)),
+    # 1024 rows per KV head: four 256-row units that share the KV head
+    "mini_mqa_d15": Workload("mini_mqa_d15", 2008, B=2, H_q=64, H_kv=1, hd=128, D=15,
+                             T_range=(100, 700)),
     "mini_hd64_g4": Workload("mini_hd64_g4", 2006, B=4, H_q=8, H_kv=2, hd=64, D=3,
                              T_range=(0, 1000), V=333, p_match=0.7),
     "mini_fp8_hd64": Workload("mini_fp8_hd64", 2007, B=2, H_q=4, H_kv=1, hd=64, D=5,
