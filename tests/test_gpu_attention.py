@@ -100,6 +100,30 @@ def test_fp8_several_row_units_per_kv_head(H_q, H_kv, D, split):
     check(gpu, oracle_for(inp), f"{w.name}/split={split}")
 
 
+# Head dim 64 in every row-unit form of the stream-K kernels: one 256-row unit per KV
+# head (136 and 192 rows), two 256-row units (512 rows), two 128-row units (256 rows),
+# and e4m3 caches with two and four 128-row units.
+HD64_UNITS = [("bf16", 8, 2, 16), ("bf16", 8, 2, 23), ("bf16", 32, 1, 15), ("bf16", 16, 2, 15),
+              ("fp8_e4m3", 16, 2, 15), ("fp8_e4m3", 32, 1, 15)]
+
+
+def hd64_units_workload(kv, G, H_kv, D):
+    return MINI["mini_hd64_g4"].replace(name=f"hd64_g{G}_kv{H_kv}_d{D}_{kv}", H_q=G * H_kv,
+                                        H_kv=H_kv, D=D, kv_dtype=kv, T_range=(50, 1500))
+
+
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("kv,G,H_kv,D", HD64_UNITS,
+                         ids=lambda v: str(v) if not isinstance(v, str) else v)
+def test_hd64_row_units_all_elements(kv, G, H_kv, D, split):
+    w = hd64_units_workload(kv, G, H_kv, D)
+    assert w.hd == 64 and w.M > 128
+    inp = make_attn_inputs(w)
+    gpu = run_attention(inp, split_tokens=split)
+    assert np.isfinite(gpu).all()
+    check(gpu, oracle_for(inp), f"{w.name}/split={split}")
+
+
 def test_tiny_contiguous_exact_shape():
     inp = make_attn_inputs(TINY)
     assert inp.kv_lens.tolist() == [260] and (inp.block_table[0, :17] == np.arange(17)).all()

@@ -82,6 +82,24 @@ def test_tree_attention_256_row_units(kv):
     _check(gpu, _oracle(inp, plan.parents), w.name)
 
 
+@pytest.mark.parametrize("kv,G,H_kv,D", [("bf16", 8, 2, 16), ("bf16", 32, 1, 15),
+                                         ("fp8_e4m3", 16, 2, 15)], ids=["bf16_m136", "bf16_m512",
+                                                                        "fp8_m256"])
+def test_tree_attention_hd64_row_units(kv, G, H_kv, D):
+    """Head dim 64 with one or two 256-row units per KV head (bf16) and two 128-row
+    units (e4m3): random trees against the oracle, and a chain tree bit for bit
+    against spec_verify_attn."""
+    w = MINI["mini_hd64_g4"].replace(name=f"tree_hd64_g{G}_d{D}_{kv}", H_q=G * H_kv, H_kv=H_kv,
+                                     D=D, kv_dtype=kv, T_range=(50, 1500))
+    inp = make_attn_inputs(w)
+    plan = make_tree_plan(w, shape="random", width=4)
+    gpu = DeviceAttn.to_f64(run_tree_attention(inp, plan.masks)[0])
+    _check(gpu, _oracle(inp, plan.parents), w.name)
+    chain = make_tree_plan(w, shape="chain")
+    tree_out, d = run_tree_attention(inp, chain.masks)
+    assert torch.equal(tree_out, d.run())
+
+
 def test_tree_attention_64_nodes():
     w = EDGE["edge_d63"]
     inp = make_attn_inputs(w)
