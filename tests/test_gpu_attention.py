@@ -212,15 +212,15 @@ def _batch2100_inputs(hd, G, D, kv):
 
 
 # More than 2048 sequences take the split-K path (partial kernels + combine):
-# M = 16 rows per KV head runs the direct kernel, M = 128 the LDS ring (bf16)
-# or the register-staged kernel (e4m3).  Contexts start at 32 tokens: with
+# M = 16 and 64 rows per KV head run the direct kernel (one and two waves per
+# workgroup), M = 128 the LDS ring (bf16) or the register-staged kernel (e4m3).  Contexts start at 32 tokens: with
 # only a handful of keys an output row is hardly an average (|O| near 3), and
 # its bf16 rounding alone would use most of the 1e-2 bar.  With 256-token
 # splits the long contexts span several splits, so the combine kernel merges
 # partial results; the automatic split size is the planner's own choice.
 @pytest.mark.parametrize("split", [256, 0], ids=["split256", "auto"])
 @pytest.mark.parametrize("kv", [KV_BF16, KV_FP8], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("G,D", [(4, 3), (8, 15)], ids=["m16", "m128"])
+@pytest.mark.parametrize("G,D", [(4, 3), (8, 7), (8, 15)], ids=["m16", "m64", "m128"])
 @pytest.mark.parametrize("hd", [64, 128])
 def test_split_path_above_2048_sequences(hd, G, D, kv, split):
     inp = _batch2100_inputs(hd, G, D, kv)

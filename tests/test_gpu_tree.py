@@ -83,12 +83,12 @@ def test_tree_attention_256_row_units(kv):
 
 
 @pytest.mark.parametrize("kv,G,H_kv,D", [("bf16", 8, 2, 16), ("bf16", 32, 1, 15),
-                                         ("fp8_e4m3", 16, 2, 15)], ids=["bf16_m136", "bf16_m512",
-                                                                        "fp8_m256"])
+                                         ("bf16", 16, 2, 15), ("fp8_e4m3", 16, 2, 15)],
+                         ids=["bf16_m136", "bf16_m512", "bf16_m256", "fp8_m256"])
 def test_tree_attention_hd64_row_units(kv, G, H_kv, D):
     """Head dim 64 with one or two 256-row units per KV head (bf16) and two 128-row
-    units (e4m3): random trees against the oracle, and a chain tree bit for bit
-    against spec_verify_attn."""
+    units (bf16 and e4m3): random trees against the oracle, and a chain tree bit for
+    bit against spec_verify_attn."""
     w = MINI["mini_hd64_g4"].replace(name=f"tree_hd64_g{G}_d{D}_{kv}", H_q=G * H_kv, H_kv=H_kv,
                                      D=D, kv_dtype=kv, T_range=(50, 1500))
     inp = make_attn_inputs(w)
@@ -138,7 +138,7 @@ def _tree_batch2100_inputs(hd, G, D, kv):
 
 
 # More than 2048 sequences: tree masks on the split-K path (direct kernel for
-# M = 16, the LDS ring or the register-staged kernel for M = 128), 256-token
+# M = 16 and 64, the LDS ring or the register-staged kernel for M = 128), 256-token
 # splits and the automatic choice.  Mostly short contexts with every 64th one
 # long (1000 to 2000 tokens); every 97th is shorter than one 32-key sub-block
 # (1 to 31 tokens), so whole tiles, even whole splits, hold only new positions
@@ -147,7 +147,7 @@ def _tree_batch2100_inputs(hd, G, D, kv):
 # rounding alone is up to 2^-9 |O|: they are held to max-abs 1e-2 + 2^-8 |O|.
 @pytest.mark.parametrize("split", [256, 0], ids=["split256", "auto"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("G,D", [(4, 3), (8, 15)], ids=["m16", "m128"])
+@pytest.mark.parametrize("G,D", [(4, 3), (8, 7), (8, 15)], ids=["m16", "m64", "m128"])
 @pytest.mark.parametrize("hd", [64, 128])
 def test_tree_attention_split_path(hd, G, D, kv, split):
     inp, plan = _tree_batch2100_inputs(hd, G, D, kv)
