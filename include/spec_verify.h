@@ -142,8 +142,10 @@ sv_status spec_verify_attn_workspace_size(const sv_attn_params* p, size_t* bytes
  * Size limits (SV_ERR_UNSUPPORTED beyond them): B*R*H_q*hd < 2^31 elements;
  * H_kv*hd*32 < 2^31 (bytes of one physical block of a bf16 cache, all KV
  * heads); num_blocks*H_kv < 2^32 (entries of a scale array); for B <= 2048,
- * B*H_kv*ceil(M/128)*ceil(max_kv_len/32) < 2^31 (32-key tiles of the whole
- * batch, M = G*R rows per KV head; 256 rows per tile when 128 < M < 256).
+ * B*H_kv*U*ceil(max_kv_len/32) < 2^31 (32-key tiles of the whole batch), with
+ * M = G*R rows per KV head and U its row units: ceil(M/256) for a bf16 cache
+ * with M > 128, M != 256 and M mod 256 either 0 or above 128, else
+ * ceil(M/128).
  *
  * Device preconditions: R <= kv_lens[b] <= max_kv_len; block_table[b][j] in
  * [0, num_blocks) for j < ceil(kv_lens[b] / 16).  The other entries of the
